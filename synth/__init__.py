@@ -1,0 +1,92 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the smoke check.
+
+Nothing in here quantises, multiplies or scales: it only draws random numbers
+and builds index arrays, so both the CPU oracle and the HIP path can consume
+the same bytes without sharing any of the method's arithmetic.
+
+Recipe (the pages measure DeepSeek-V3/R1 inference shapes but name no input
+distribution, so i.i.d. N(0,1) values stand in for activations and weights):
+* values: numpy default_rng(seed).standard_normal(shape, float32), then RNE to
+  bf16 (torch's CPU cast), stored as uint16 bit patterns;
+* seeds: A = 1000 + workload number, B = 2000 + workload number;
+* contiguous m_indices: expert g repeated for its (128-aligned) segment;
+* masked_m: default_rng(3000).integers(1, M_max + 1, size=G).
+"""
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+SEED_A = 1000
+SEED_B = 2000
+SEED_MASK = 3000
+
+
+def bf16_normal(shape, seed: int, scale: float = 1.0) -> np.ndarray:
+    """i.i.d. N(0, scale^2) values rounded to bf16, as uint16 bit patterns."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if scale != 1.0:
+        x *= np.float32(scale)
+    t = torch.from_numpy(x).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def contiguous_m_indices(segment_rows, pad_rows=None, order=None) -> np.ndarray:
+    """Per-row expert ids for the contiguous layout.
+
+    segment_rows[g] rows for expert g, followed by pad_rows[g] rows of -1
+    (padding up to the alignment).  `order` permutes the experts' segments.
+    """
+    groups = len(segment_rows)
+    pad_rows = pad_rows or [0] * groups
+    order = list(range(groups)) if order is None else list(order)
+    parts = []
+    for g in order:
+        parts.append(np.full(segment_rows[g], g, dtype=np.int32))
+        parts.append(np.full(pad_rows[g], -1, dtype=np.int32))
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int32)
+
+
+def masked_m(groups: int, m_max: int, seed: int = SEED_MASK) -> np.ndarray:
+    """Valid-row counts per expert, uniform in [1, m_max]."""
+    return np.random.default_rng(seed).integers(1, m_max + 1, size=groups).astype(np.int32)
+
+
+@dataclass
+class Workload:
+    """One benchmark workload: layout and sizes, plus its seeds."""
+
+    name: str
+    layout: str  # "dense" | "contiguous" | "masked"
+    m: int  # rows per group (dense: M; contiguous: rows per expert; masked: M_max)
+    n: int
+    k: int
+    groups: int = 1
+    number: int = 0
+    note: str = ""
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def seed_a(self) -> int:
+        return SEED_A + self.number
+
+    @property
+    def seed_b(self) -> int:
+        return SEED_B + self.number
+
+
+NK_PAIRS = [(2112, 7168), (24576, 1536), (32768, 512), (7168, 16384), (4096, 7168), (7168, 2048)]
+
+
+def workloads():
+    """The five workloads of the DeepSeek-V3 shapes this library is measured on."""
+    out = [Workload("dense_m64_n2112_k7168", "dense", 64, 2112, 7168, number=1)]
+    for n, k in NK_PAIRS:
+        out.append(Workload(f"dense_m128_n{n}_k{k}", "dense", 128, n, k, number=2))
+    for n, k in NK_PAIRS:
+        out.append(Workload(f"dense_m4096_n{n}_k{k}", "dense", 4096, n, k, number=3))
+    out.append(Workload("contiguous_g4_m8192_n4096_k7168", "contiguous", 8192, 4096, 7168, groups=4, number=4))
+    out.append(Workload("masked_g4_mmax1024_n4096_k7168", "masked", 1024, 4096, 7168, groups=4, number=5))
+    return out

@@ -1,0 +1,35 @@
+"""The bf16-output parity rule used by every GEMM comparison.
+
+Reference = the oracle's fp64 result D64 (not its bf16 rounding), over the
+rows the method writes.  A GPU result c passes when
+    ||c - D64||_2 / ||D64||_2 <= 2e-3, and
+    |c - D64| <= 1e-2 * rms(D64) + 2^-8 * |D64| for every element.
+bf16 rounding of the exact result alone gives a relative L2 error of about
+1.7e-3 on N(0,1) inputs, so the rule leaves room for fp32 accumulation in any
+order and nothing more.
+"""
+
+import numpy as np
+
+REL_L2 = 2e-3
+ABS_RMS = 1e-2
+REL_ELT = 2.0 ** -8
+
+
+def check(c, ref, what=""):
+    c = np.asarray(c, dtype=np.float64).ravel()
+    ref = np.asarray(ref, dtype=np.float64).ravel()
+    assert c.shape == ref.shape, what
+    if ref.size == 0:
+        return {"rel_l2": 0.0, "worst": 0.0}
+    assert np.all(np.isfinite(c)), f"{what}: non-finite output"
+    norm = np.linalg.norm(ref)
+    rms = norm / np.sqrt(ref.size)
+    diff = np.abs(c - ref)
+    rel_l2 = np.linalg.norm(c - ref) / norm if norm > 0 else np.linalg.norm(c - ref)
+    bound = ABS_RMS * rms + REL_ELT * np.abs(ref)
+    worst = float(np.max(diff / np.where(bound > 0, bound, 1.0)))
+    bad = int(np.count_nonzero(diff > bound))
+    assert rel_l2 <= REL_L2 or norm == 0, f"{what}: rel-L2 {rel_l2:.3e} > {REL_L2}"
+    assert bad == 0, f"{what}: {bad} elements outside the per-element bound (worst ratio {worst:.3f})"
+    return {"rel_l2": float(rel_l2), "worst": worst}
