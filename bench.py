@@ -1,0 +1,384 @@
+#!/usr/bin/env python3
+"""Benchmark of the fine-grained-scaled FP8 GEMM path on one MI355X.
+
+One step = one pass of the hot path over one batch of synthetic input: for
+every shape of the workload, quantise the bf16 activations per 1x128 tile
+(dg_quant_1x128) and run the GEMM (dg_fp8_gemm_nt, or the grouped entry
+points) on weights that were quantised per 128x128 block once, before timing
+(weights are converted offline, once per weight).
+
+The default workload is the dense decode sweep M = 128 over the six (N, K)
+pairs of DeepSeek-V3 shapes.  `--workload all` also measures every other
+workload shape (one line per shape on stderr, and a per-shape table in the
+JSON line).
+
+Throughput accounting (the pages' own, which reproduces every row of the
+DeepGEMM performance tables, see tests/golden/):
+    flops = 2 * M_valid * N * K
+    bytes = M_valid * K + G * N * K + 2 * M_valid * N   (fp8 A, fp8 B, bf16 D)
+Scale bytes are reported separately.
+
+Caches: every weight matrix is rotated through enough copies that the set
+touched per step exceeds twice the 256 MB Infinity Cache, so weights come
+from HBM, not from the L2s or MALL.
+"""
+
+import argparse
+import json
+import math
+import os
+import platform
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (no sparsity)
+MALL_BYTES = 256 << 20
+METRIC = "FP8 TFLOPS and HBM GB/s per shape, % of MI355X FP8/HBM roofline"
+
+# DeepGEMM performance tables (H800), TFLOPS per (layout, groups, m, n, k):
+# DeepGEMM project introduction, section Performance.  Used only as context.
+PAGES_TFLOPS = {
+    ("dense", 1, 128, 2112, 7168): 352, ("dense", 1, 128, 24576, 1536): 535,
+    ("dense", 1, 128, 32768, 512): 358, ("dense", 1, 128, 7168, 16384): 645,
+    ("dense", 1, 128, 4096, 7168): 533, ("dense", 1, 128, 7168, 2048): 510,
+}
+
+
+def algorithmic_flops(m_valid, n, k):
+    return 2.0 * m_valid * n * k
+
+
+def algorithmic_bytes(m_valid, n, k, groups=1):
+    return float(m_valid * k + groups * n * k + 2 * m_valid * n)
+
+
+def scale_bytes(m_valid, n, k, groups=1):
+    return float(4 * m_valid * (k // 128) + 4 * groups * ((n + 127) // 128) * (k // 128))
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="decode128",
+                   help="decode128 (default) | all | a workload name from synth.workloads()")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work for the oracle sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run only a plain device copy of known size (for counter calibration)")
+    return p.parse_args(argv)
+
+
+# --------------------------------------------------------------- workloads --
+
+def select_workloads(name):
+    import synth
+    wls = synth.workloads()
+    if name == "decode128":
+        return [w for w in wls if w.layout == "dense" and w.m == 128]
+    if name == "all":
+        return wls
+    pick = [w for w in wls if w.name == name]
+    if not pick:
+        raise SystemExit(f"unknown workload {name}; choose from decode128, all, " + ", ".join(w.name for w in wls))
+    return pick
+
+
+class Prepared:
+    """Device buffers for one workload shape, weights rotated for cache misses."""
+
+    def __init__(self, dg, torch, wl):
+        import synth
+        self.wl = wl
+        g, n, k = wl.groups, wl.n, wl.k
+        dev = "cuda"
+        if wl.layout == "dense":
+            self.m_rows, a_shape = wl.m, (wl.m, k)
+        elif wl.layout == "contiguous":
+            self.m_rows, a_shape = g * wl.m, (g * wl.m, k)
+        else:
+            self.m_rows, a_shape = wl.m, (g, wl.m, k)
+        xa = synth.bf16_normal(a_shape, wl.seed_a)
+        self.x = torch.from_numpy(xa.view(np.int16)).to(dev)
+        self.a = torch.empty(a_shape, dtype=torch.uint8, device=dev)
+        ld = dg.dg_get_sf_leading_dim(self.m_rows)
+        self.sfa = torch.empty(((g,) if wl.layout == "masked" else ()) + (k // 128, ld), dtype=torch.float32, device=dev)
+        b_shape = (n, k) if wl.layout == "dense" else (g, n, k)
+        xb = torch.from_numpy(synth.bf16_normal(b_shape, wl.seed_b).view(np.int16)).to(dev)
+        qb = torch.empty(b_shape, dtype=torch.uint8, device=dev)
+        sfb = torch.empty(((g,) if wl.layout != "dense" else ()) + ((n + 127) // 128, k // 128), dtype=torch.float32, device=dev)
+        dg.dg_quant_128x128(xb, qb, sfb)
+        del xb
+        set_bytes = qb.numel() + sfb.numel() * 4
+        copies = max(1, math.ceil(2 * MALL_BYTES / set_bytes)) if set_bytes < 2 * MALL_BYTES else 1
+        copies = min(copies, 64)
+        self.b = [qb] + [qb.clone() for _ in range(copies - 1)]
+        self.sfb = [sfb] + [sfb.clone() for _ in range(copies - 1)]
+        self.d = torch.empty(((g,) if wl.layout == "masked" else ()) + (self.m_rows, n), dtype=torch.int16, device=dev)
+        self.mi = None
+        self.mm = None
+        if wl.layout == "contiguous":
+            self.mi = torch.from_numpy(synth.contiguous_m_indices([wl.m] * g)).to(dev)
+            self.m_valid = g * wl.m
+        elif wl.layout == "masked":
+            mm = synth.masked_m(g, wl.m)
+            self.mm = torch.from_numpy(mm).to(dev)
+            self.m_valid = int(mm.sum())
+        else:
+            self.m_valid = wl.m
+        ws = dg.dg_get_workspace_size(self.m_rows, n, k, g)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
+        self.flops = algorithmic_flops(self.m_valid, n, k)
+        self.bytes = algorithmic_bytes(self.m_valid, n, k, g)
+        self.sf_bytes = scale_bytes(self.m_valid, n, k, g)
+        layout_id = {"dense": 0, "contiguous": 1, "masked": 2}[wl.layout]
+        self.config = dg.dg_describe_config(layout_id, self.m_rows, n, k, g, dg.dg_get_num_cus())
+        self.kernel_key = self.config.split(" workspace=")[0]
+
+    def quant(self, dg):
+        dg.dg_quant_1x128(self.x, self.a, self.sfa)
+
+    def gemm(self, dg, r):
+        b, sfb = self.b[r % len(self.b)], self.sfb[r % len(self.sfb)]
+        if self.wl.layout == "dense":
+            dg.dg_fp8_gemm_nt(self.a, self.sfa, b, sfb, self.d, workspace=self.ws)
+        elif self.wl.layout == "contiguous":
+            dg.dg_grouped_contiguous(self.a, self.sfa, b, sfb, self.d, self.mi, workspace=self.ws)
+        else:
+            dg.dg_grouped_masked(self.a, self.sfa, b, sfb, self.d, self.mm, expected_m=self.m_valid // self.wl.groups,
+                                 workspace=self.ws)
+
+
+# ------------------------------------------------------------------ timing --
+
+def time_steps(dg, torch, preps, steps, warmup):
+    """Time `steps` whole steps; GEMM launches are bracketed by events too."""
+    stream = torch.cuda.current_stream()
+    for w in range(warmup):
+        for p in preps:
+            p.quant(dg)
+            p.gemm(dg, w)
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in preps] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(steps):
+        for i, p in enumerate(preps):
+            p.quant(dg)
+            ev[s][i][0].record(stream)
+            p.gemm(dg, warmup + s)
+            ev[s][i][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    gemm_ms = np.array([[a.elapsed_time(b) for (a, b) in row] for row in ev])  # [steps][shapes]
+    return total_ms, gemm_ms
+
+
+def time_quant(dg, torch, p, reps=20):
+    stream = torch.cuda.current_stream()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p.quant(dg)
+    torch.cuda.synchronize()
+    s.record(stream)
+    for _ in range(reps):
+        p.quant(dg)
+    e.record(stream)
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+# ------------------------------------------------------------ CPU baseline --
+
+def cpu_baseline(wls, target_s):
+    """The oracle, single-threaded, on a bounded sample of the workload.
+
+    Sample: for each shape, the full M rows of A against the first 512 columns
+    of B (four 128-row weight blocks), quantising both from bf16 like the GPU
+    step does (the weight quantisation is excluded from the GPU step, so it is
+    excluded here too).  Shapes are visited in order until about target_s
+    seconds of work are done.  Rate = sample flops / oracle seconds.
+    """
+    import synth
+    from oracle import gemm, quant
+    from threadpoolctl import threadpool_limits
+
+    flops = 0.0
+    secs = 0.0
+    done = []
+    with threadpool_limits(limits=1):
+        for wl in wls:
+            m = wl.m if wl.layout == "dense" else min(wl.m, 256)
+            ncols = min(wl.n, 512)
+            xa = synth.bf16_normal((m, wl.k), wl.seed_a)
+            xb = synth.bf16_normal((ncols, wl.k), wl.seed_b)
+            qb, sfb = quant.quant_128x128(xb)
+            t0 = time.perf_counter()
+            qa, sfa = quant.quant_1x128(xa)
+            gemm.gemm_nt_ref(qa, sfa, qb, sfb)
+            secs += time.perf_counter() - t0
+            flops += algorithmic_flops(m, ncols, wl.k)
+            done.append(f"{wl.name}[:{m}, :{ncols}]")
+            if secs >= target_s:
+                break
+    return {
+        "value": flops / secs / 1e12,
+        "unit": "TFLOPS",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "single-threaded numpy oracle (quantise A per 1x128 + fp64 blockwise GEMM) on "
+                  + ", ".join(done) + f"; {secs:.1f} s of CPU work",
+        "cpu_model": platform.processor() or _cpu_model(),
+        "host_cores": os.cpu_count(),
+    }
+
+
+def _cpu_model():
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# -------------------------------------------------------------------- main --
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the library has no multi-GPU path).", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    import moe_grouped_gemm_02_amd as dg
+
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": src.numel(), "launches": 5}))
+        return 0
+
+    wls = select_workloads(args.workload)
+    headline = [w for w in wls if w.layout == "dense" and w.m == 128] or wls
+    preps = [Prepared(dg, torch, w) for w in headline]
+    torch.cuda.synchronize()
+
+    total_ms, gemm_ms = time_steps(dg, torch, preps, args.steps, args.warmup)
+    ms_per_step = total_ms / args.steps
+    step_flops = sum(p.flops for p in preps)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    per_shape = []
+    for i, p in enumerate(preps):
+        t = float(np.mean(gemm_ms[:, i])) * 1e-3
+        per_shape.append(shape_record(p, t, time_quant(dg, torch, p)))
+
+    extra = []
+    if args.workload == "all":
+        for w in wls:
+            if w in headline:
+                continue
+            p = Prepared(dg, torch, w)
+            _, g_ms = time_steps(dg, torch, [p], max(5, args.steps // 2), 2)
+            extra.append(shape_record(p, float(np.mean(g_ms[:, 0])) * 1e-3, time_quant(dg, torch, p)))
+            print(json.dumps(extra[-1]), file=sys.stderr, flush=True)
+            del p
+            torch.cuda.empty_cache()
+
+    # Dominant kernel: the GEMM configuration with the most total time.
+    by_kernel = {}
+    for i, p in enumerate(preps):
+        by_kernel.setdefault(p.kernel_key, []).append(i)
+    key = max(by_kernel, key=lambda k_: sum(float(np.sum(gemm_ms[:, i])) for i in by_kernel[k_]))
+    idx = by_kernel[key]
+    mean_bytes = float(np.mean([preps[i].bytes for i in idx]))
+    mean_dur = float(np.mean(gemm_ms[:, idx])) * 1e-3
+    achieved = mean_bytes / mean_dur / 1e9
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": None,
+        "kernel": key,
+        "launches_averaged": len(idx) * args.steps,
+        "mean_algorithmic_bytes_per_launch": mean_bytes,
+        "mean_launch_us": round(mean_dur * 1e6, 3),
+    }
+
+    page_t = sum(2.0 * w.m * w.n * w.k / (PAGES_TFLOPS[("dense", 1, w.m, w.n, w.k)] * 1e12)
+                 for w in headline if ("dense", 1, w.m, w.n, w.k) in PAGES_TFLOPS)
+    vs = None
+    if headline and all(("dense", 1, w.m, w.n, w.k) in PAGES_TFLOPS for w in headline):
+        vs = round(value / (step_flops / page_t / 1e12), 4)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": vs,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": "dense_decode_sweep_m128" if len(headline) > 1 else headline[0].name,
+            "m": headline[0].m,
+            "nk_pairs": [[w.n, w.k] for w in headline],
+            "step": "dg_quant_1x128(A) + GEMM per shape; weights quantised once before timing",
+            "weight_rotation_copies": [len(p.b) for p in preps],
+            "num_cus": dg.dg_get_num_cus(),
+        },
+        "step_gbps": round(sum(p.bytes for p in preps) / (ms_per_step * 1e-3) / 1e9, 1),
+        "roofline": roofline,
+        "per_shape": per_shape + extra,
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(headline, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def shape_record(p, t, quant_ms):
+    tflops = p.flops / t / 1e12
+    gbps = p.bytes / t / 1e9
+    return {
+        "workload": p.wl.name,
+        "layout": p.wl.layout,
+        "groups": p.wl.groups,
+        "m_valid": p.m_valid,
+        "n": p.wl.n,
+        "k": p.wl.k,
+        "gemm_us": round(t * 1e6, 3),
+        "tflops": round(tflops, 2),
+        "gbps": round(gbps, 1),
+        "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
+        "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "scale_bytes": p.sf_bytes,
+        "quant_1x128_us": round(quant_ms * 1e3, 3),
+        "config": p.config,
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,186 @@
+/*
+ * dg.h - C ABI of libdg: fine-grained-scaled FP8 GEMM for AMD MI355X (gfx950).
+ *
+ * What is computed (DeepGEMM project introduction, docs.beyondata.com,
+ * sections Interfaces, Grouped GEMM (contiguous layout) and Grouped GEMM
+ * (masked layout); "Deepseek DeepGEMM technical principles", blog.51cto.com,
+ * section "Technical background and core principles"):
+ *
+ *   D[m][n] = bf16( sum_kb  P_kb[m][n] * (sfa[kb][m] * sfb[n/128][kb]) )
+ *   P_kb[m][n] = sum_{k in slice kb} e4m3(A[m][k]) * e4m3(B[n][k])
+ *
+ * A is [M][K] and B is [N][K] (the "NT" layout: both K-contiguous), both
+ * OCP e4m3fn bytes.  Activations carry one fp32 scale per 1x128 tile, weights
+ * one per 128x128 block.  Each 128-wide K slice is a low-precision partial
+ * product that is scaled and promoted into an fp32 accumulator; the output is
+ * bf16 (round to nearest even).
+ *
+ * Conventions for every entry point
+ *   - All data pointers are DEVICE pointers on the current HIP device; the
+ *     caller allocates and owns every buffer (including any workspace).  The
+ *     library allocates nothing per call and never synchronises the host.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream); all
+ *     work is enqueued on it asynchronously.
+ *   - e4m3 = uint8_t (OCP e4m3fn, max 448), bf16 = uint16_t bit patterns.
+ *   - Argument errors are detected on the host before anything is launched and
+ *     returned as a negative dg_status; nothing is enqueued in that case.
+ *     A launch failure returns DG_ERR_HIP.  The text of the last error on the
+ *     calling thread is available from dg_get_last_error_string().
+ *   - The output must not alias any input.
+ *   - m == 0 (or n == 0) is a successful no-op.  k == 0 writes zeros (the
+ *     empty sum); then a, b, sfa and sfb are not read and may be NULL.
+ *
+ * Shape and alignment rules (checked; DG_ERR_* on violation)
+ *   - k % 128 == 0 (DG_ERR_UNSUPPORTED_SHAPE); m, n arbitrary >= 0.
+ *   - a, b, d, sfa, sfb 16-byte aligned; lda, ldb multiples of 16 (bytes =
+ *     elements); ldd a multiple of 8 elements; ld_sfa a multiple of 4 and
+ *     >= the rows it covers (DG_ERR_MISALIGNED / DG_ERR_INVALID_VALUE).
+ */
+#ifndef DG_H_
+#define DG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DG_SUCCESS = 0,
+  DG_ERR_INVALID_VALUE = -1,    /* null pointer, negative size, bad leading dim */
+  DG_ERR_UNSUPPORTED_SHAPE = -2,/* k % 128 != 0, contiguous m_total % 128 != 0, too large */
+  DG_ERR_MISALIGNED = -3,       /* pointer or stride not 16-byte aligned */
+  DG_ERR_WORKSPACE = -4,        /* workspace smaller than dg_get_workspace_size() */
+  DG_ERR_HIP = -5               /* a HIP runtime call or kernel launch failed */
+} dg_status;
+
+/* ---------------------------------------------------------------- GEMMs -- */
+
+/*
+ * Dense NT GEMM (gemm_fp8_fp8_bf16_nt; project introduction, section
+ * Interfaces, "Normal dense GEMM (non-grouped)").
+ *   a   [m][lda]  e4m3, row r's K values at a + r*lda
+ *   sfa [k/128][ld_sfa] fp32, MN-major ("TMA-aligned and transposed" in the
+ *       pages; here ld_sfa = round_up(m, 4), see dg_get_sf_leading_dim)
+ *   b   [n][ldb]  e4m3
+ *   sfb [ceil(n/128)][k/128] fp32 (the last row block may be partial)
+ *   d   [m][ldd]  bf16 output; only columns < n of rows < m are written
+ *   workspace: device scratch of at least dg_get_workspace_size(m, n, k, 1)
+ *       bytes (may be NULL when that size is 0); contents need not be
+ *       initialised and are clobbered.
+ */
+int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
+                   int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Grouped GEMM, contiguous layout (m_grouped_gemm_fp8_fp8_bf16_nt_contiguous;
+ * project introduction, section "Grouped GEMM (contiguous layout)"): the
+ * tokens of all experts are concatenated along M; only M is grouped, N and K
+ * are shared.
+ *   a   [m_total][k] e4m3, sfa [k/128][ld_sfa] fp32 (ld_sfa >= m_total)
+ *   b   [num_groups][n][k] e4m3, sfb [num_groups][ceil(n/128)][k/128] fp32
+ *   d   [m_total][n] bf16
+ *   m_indices [m_total] int32 (device): expert of each row.
+ * Rules: m_total % 128 == 0 (each expert segment is aligned to the M block,
+ * dg_get_m_alignment_for_contiguous_layout()).  A row whose index is < 0 or
+ * >= num_groups is padding and is NOT written.  Within each aligned 128-row
+ * block all non-padding rows must name the same expert (precondition; if it is
+ * violated, rows whose index differs from the block's largest valid index are
+ * left unwritten).  Nothing is read out of bounds for any index value.
+ */
+int dg_grouped_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
+                          const float* sfb, uint16_t* d, const int32_t* m_indices,
+                          int m_total, int n, int k, int num_groups, int64_t ld_sfa,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Grouped GEMM, masked layout (m_grouped_gemm_fp8_fp8_bf16_nt_masked; project
+ * introduction, section "Grouped GEMM (masked layout)"): used when the host
+ * does not know how many tokens each expert received (graph-captured decode),
+ * so the valid-row counts live on the device and only the valid part is
+ * computed.
+ *   a   [num_groups][m_max][k] e4m3
+ *   sfa [num_groups][k/128][ld_sfa] fp32 (ld_sfa >= m_max)
+ *   b   [num_groups][n][k] e4m3, sfb [num_groups][ceil(n/128)][k/128] fp32
+ *   d   [num_groups][m_max][n] bf16
+ *   masked_m [num_groups] int32 (device): valid rows per group, clamped to
+ *       [0, m_max].  Rows >= masked_m[g] of group g are NOT written.
+ *   expected_m: host hint of the typical masked_m (used only to pick tile
+ *       sizes; any value >= 0 is valid, 0 = unknown).
+ */
+int dg_grouped_masked(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                      uint16_t* d, const int32_t* masked_m, int num_groups, int m_max, int n,
+                      int k, int expected_m, int64_t ld_sfa, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------- quantisers -- */
+
+/*
+ * Activation quantiser, one fp32 scale per 1x128 tile ("Deepseek DeepGEMM
+ * technical principles", section "Technical background and core principles";
+ * fp32 scales per the yfxerp.com DeepGEMM article, section 3.1).  For each row
+ * r and 128-column slice j of x (bf16 widened exactly to fp32):
+ *   amax = max |x|,  s = fp32(amax / 448)  (IEEE division, round to nearest),
+ *   q = e4m3( fp32(x / s) )  (nearest, ties to even, magnitudes above 448
+ *   clamp to 448; an all-zero tile gets s = 0 and signed-zero codes).
+ *   x  [num_groups][rows][cols] bf16 (row-major, contiguous)
+ *   q  [num_groups][rows][cols] e4m3
+ *   sf [num_groups][cols/128][ld_sf] fp32 (MN-major); entries for rows in
+ *      [rows, ld_sf) are written as 0.
+ * cols % 128 == 0; ld_sf >= rows and a multiple of 4.  num_groups >= 1 (use
+ * num_groups > 1 for the masked layout's [G][M_max][K] activations).
+ */
+int dg_quant_1x128(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
+                   int64_t ld_sf, int num_groups, void* stream);
+
+/*
+ * Weight quantiser, one fp32 scale per 128x128 block (same sources and the
+ * same arithmetic as dg_quant_1x128, with amax over the block; when rows is
+ * not a multiple of 128 the last block covers only the valid rows).
+ *   w  [num_groups][rows][cols] bf16, q [num_groups][rows][cols] e4m3
+ *   sf [num_groups][ceil(rows/128)][cols/128] fp32
+ * cols % 128 == 0.
+ */
+int dg_quant_128x128(const uint16_t* w, uint8_t* q, float* sf, int rows, int cols,
+                     int num_groups, void* stream);
+
+/* -------------------------------------------------------------- utilities -- */
+
+/* Workspace bytes a GEMM of this shape needs (0 when it needs none).  For the
+ * masked layout pass m = m_max; for contiguous pass m = m_total. */
+size_t dg_get_workspace_size(int m, int n, int k, int num_groups);
+
+/* Number of compute units the persistent kernels are sized to (set_num_sms /
+ * get_num_sms; project introduction, section Utility functions).  The default
+ * is the device's CU count, or DG_NUM_CUS from the environment.
+ * dg_get_num_cus returns a negative dg_status if no device can be queried;
+ * dg_set_num_cus(0) restores the default. */
+int dg_get_num_cus(void);
+int dg_set_num_cus(int num_cus);
+
+/* Row alignment each expert segment needs in the contiguous layout
+ * (get_m_alignment_for_contiguous_layout; section Utility functions): 128. */
+int dg_get_m_alignment_for_contiguous_layout(void);
+
+/* Leading dimension of the transposed activation scale matrix for m rows
+ * (get_tma_aligned_size; section Utility functions): round_up(m, 4), so that
+ * every column starts 16-byte aligned.  Returns -1 for m < 0. */
+int64_t dg_get_sf_leading_dim(int m);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char* dg_get_last_error_string(void);
+
+/* Human-readable description of the tile configuration the library would
+ * choose for a GEMM (layout 0 = dense, 1 = contiguous, 2 = masked), written
+ * into buf (NUL-terminated, truncated to len).  Returns DG_SUCCESS or an
+ * error for invalid arguments.  Pure host logic: needs no device. */
+int dg_describe_config(int layout, int m, int n, int k, int num_groups, int num_cus,
+                       char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H_ */

@@ -1,0 +1,240 @@
+"""Python binding of libdg (fine-grained-scaled FP8 GEMM for MI355X / gfx950).
+
+Argument marshalling only: every function here checks tensor devices, dtypes
+and shapes, then calls the C entry point of the same name with raw device
+pointers and the current HIP stream.  All computation happens in the HIP
+kernels of libdg.so; there is no fallback.  Importing this package fails if
+the library has not been built (see build.py).
+
+Tensor conventions (torch dtypes standing in for the C types):
+  e4m3 codes     torch.uint8       bf16 values  torch.bfloat16 (or int16 bits)
+  fp32 scales    torch.float32     ids/counts   torch.int32
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdg.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libdg.so is not built ({LIB_PATH}); run moe_grouped_gemm_02_amd/build.py")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_L = ctypes.c_int64
+_S = ctypes.c_size_t
+
+_SIGNATURES = {
+    "dg_fp8_gemm_nt": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _L, _L, _P, _S, _P]),
+    "dg_grouped_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _P, _S, _P]),
+    "dg_grouped_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _P, _S, _P]),
+    "dg_quant_1x128": (_I, [_P, _P, _P, _I, _I, _L, _I, _P]),
+    "dg_quant_128x128": (_I, [_P, _P, _P, _I, _I, _I, _P]),
+    "dg_get_workspace_size": (_S, [_I, _I, _I, _I]),
+    "dg_get_num_cus": (_I, []),
+    "dg_set_num_cus": (_I, [_I]),
+    "dg_get_m_alignment_for_contiguous_layout": (_I, []),
+    "dg_get_sf_leading_dim": (_L, [_I]),
+    "dg_get_last_error_string": (ctypes.c_char_p, []),
+    "dg_describe_config": (_I, [_I, _I, _I, _I, _I, _I, ctypes.c_char_p, _S]),
+}
+for _name, (_res, _args) in _SIGNATURES.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGNATURES)
+
+LAYOUT_DENSE, LAYOUT_CONTIGUOUS, LAYOUT_MASKED = 0, 1, 2
+
+
+class DGError(RuntimeError):
+    """A libdg call returned a negative status."""
+
+    def __init__(self, fn, status):
+        msg = _lib.dg_get_last_error_string().decode()
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+        self.status = status
+
+
+def _check(fn, status):
+    if status != 0:
+        raise DGError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _expect(t, name, dtypes, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, has {t.dim()}")
+
+
+_U8 = (torch.uint8, torch.float8_e4m3fn)
+_BF = (torch.bfloat16, torch.int16)
+
+
+def _row_major(t, name):
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit stride in its last dimension")
+
+
+def _contig(t, name):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ------------------------------------------------------------------ GEMMs --
+
+def dg_fp8_gemm_nt(a, sfa, b, sfb, d, workspace=None):
+    """d[m][n] = bf16(A . B^T) with 1x128 (sfa [K/128][ld]) and 128x128 scales."""
+    _expect(a, "a", _U8, 2), _expect(b, "b", _U8, 2), _expect(d, "d", _BF, 2)
+    _expect(sfa, "sfa", (torch.float32,), 2), _expect(sfb, "sfb", (torch.float32,), 2)
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k or tuple(d.shape) != (m, n):
+        raise ValueError("shape mismatch between a, b and d")
+    if sfa.shape[0] != k // 128 or tuple(sfb.shape) != ((n + 127) // 128, k // 128):
+        raise ValueError("scale shapes must be sfa [K/128][ld] and sfb [ceil(N/128)][K/128]")
+    for t, nm in ((a, "a"), (b, "b"), (d, "d"), (sfa, "sfa")):
+        _row_major(t, nm)
+    _contig(sfb, "sfb")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dg_fp8_gemm_nt", _lib.dg_fp8_gemm_nt(
+        _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), m, n, k, a.stride(0), b.stride(0),
+        d.stride(0), sfa.stride(0), _ptr(workspace), ws_bytes, _stream(d)))
+    return d
+
+
+def dg_grouped_contiguous(a, sfa, b, sfb, d, m_indices, workspace=None):
+    """Contiguous grouped GEMM; b [G][N][K], m_indices [M_total] int32."""
+    _expect(a, "a", _U8, 2), _expect(b, "b", _U8, 3), _expect(d, "d", _BF, 2)
+    _expect(sfa, "sfa", (torch.float32,), 2), _expect(sfb, "sfb", (torch.float32,), 3)
+    _expect(m_indices, "m_indices", (torch.int32,), 1)
+    m_total, k = a.shape
+    groups, n = b.shape[0], b.shape[1]
+    if b.shape[2] != k or tuple(d.shape) != (m_total, n) or m_indices.shape[0] != m_total:
+        raise ValueError("shape mismatch between a, b, d and m_indices")
+    if sfa.shape[0] != k // 128 or tuple(sfb.shape) != (groups, (n + 127) // 128, k // 128):
+        raise ValueError("scale shapes must be sfa [K/128][ld] and sfb [G][ceil(N/128)][K/128]")
+    for t, nm in ((a, "a"), (b, "b"), (d, "d"), (sfb, "sfb"), (m_indices, "m_indices")):
+        _contig(t, nm)
+    _row_major(sfa, "sfa")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dg_grouped_contiguous", _lib.dg_grouped_contiguous(
+        _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), _ptr(m_indices), m_total, n, k,
+        groups, sfa.stride(0), _ptr(workspace), ws_bytes, _stream(d)))
+    return d
+
+
+def dg_grouped_masked(a, sfa, b, sfb, d, masked_m, expected_m=0, workspace=None):
+    """Masked grouped GEMM; a [G][M_max][K], sfa [G][K/128][ld], masked_m [G] int32."""
+    _expect(a, "a", _U8, 3), _expect(b, "b", _U8, 3), _expect(d, "d", _BF, 3)
+    _expect(sfa, "sfa", (torch.float32,), 3), _expect(sfb, "sfb", (torch.float32,), 3)
+    _expect(masked_m, "masked_m", (torch.int32,), 1)
+    groups, m_max, k = a.shape
+    n = b.shape[1]
+    if b.shape[0] != groups or b.shape[2] != k or tuple(d.shape) != (groups, m_max, n):
+        raise ValueError("shape mismatch between a, b and d")
+    if masked_m.shape[0] != groups:
+        raise ValueError("masked_m must have one entry per group")
+    if sfa.shape[:2] != (groups, k // 128) or tuple(sfb.shape) != (groups, (n + 127) // 128, k // 128):
+        raise ValueError("scale shapes must be sfa [G][K/128][ld] and sfb [G][ceil(N/128)][K/128]")
+    for t, nm in ((a, "a"), (b, "b"), (d, "d"), (sfa, "sfa"), (sfb, "sfb"), (masked_m, "masked_m")):
+        _contig(t, nm)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dg_grouped_masked", _lib.dg_grouped_masked(
+        _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), _ptr(masked_m), groups, m_max, n, k,
+        int(expected_m), sfa.shape[2], _ptr(workspace), ws_bytes, _stream(d)))
+    return d
+
+
+# ------------------------------------------------------------- quantisers --
+
+def dg_quant_1x128(x, q, sf):
+    """x [R][C] or [G][R][C] bf16 -> q e4m3 codes, sf [(G)][C/128][ld] fp32."""
+    _expect(x, "x", _BF), _expect(q, "q", _U8), _expect(sf, "sf", (torch.float32,))
+    if x.dim() not in (2, 3) or q.shape != x.shape or sf.dim() != x.dim():
+        raise ValueError("x, q must match and sf must have the same rank")
+    groups = 1 if x.dim() == 2 else x.shape[0]
+    rows, cols = x.shape[-2], x.shape[-1]
+    if sf.shape[-2] != cols // 128 or (x.dim() == 3 and sf.shape[0] != groups):
+        raise ValueError("sf must be [(G)][C/128][ld]")
+    for t, nm in ((x, "x"), (q, "q"), (sf, "sf")):
+        _contig(t, nm)
+    _check("dg_quant_1x128", _lib.dg_quant_1x128(
+        _ptr(x), _ptr(q), _ptr(sf), rows, cols, sf.shape[-1], groups, _stream(x)))
+    return q, sf
+
+
+def dg_quant_128x128(w, q, sf):
+    """w [N][K] or [G][N][K] bf16 -> q e4m3 codes, sf [(G)][ceil(N/128)][K/128] fp32."""
+    _expect(w, "w", _BF), _expect(q, "q", _U8), _expect(sf, "sf", (torch.float32,))
+    if w.dim() not in (2, 3) or q.shape != w.shape:
+        raise ValueError("w and q must match")
+    groups = 1 if w.dim() == 2 else w.shape[0]
+    rows, cols = w.shape[-2], w.shape[-1]
+    want = ((rows + 127) // 128, cols // 128) if w.dim() == 2 else (groups, (rows + 127) // 128, cols // 128)
+    if tuple(sf.shape) != want:
+        raise ValueError(f"sf must have shape {want}")
+    for t, nm in ((w, "w"), (q, "q"), (sf, "sf")):
+        _contig(t, nm)
+    _check("dg_quant_128x128", _lib.dg_quant_128x128(
+        _ptr(w), _ptr(q), _ptr(sf), rows, cols, groups, _stream(w)))
+    return q, sf
+
+
+# -------------------------------------------------------------- utilities --
+
+def dg_get_workspace_size(m, n, k, num_groups=1):
+    return int(_lib.dg_get_workspace_size(m, n, k, num_groups))
+
+
+def dg_get_num_cus():
+    v = _lib.dg_get_num_cus()
+    if v < 0:
+        raise DGError("dg_get_num_cus", v)
+    return v
+
+
+def dg_set_num_cus(num_cus):
+    _check("dg_set_num_cus", _lib.dg_set_num_cus(int(num_cus)))
+
+
+def dg_get_m_alignment_for_contiguous_layout():
+    return int(_lib.dg_get_m_alignment_for_contiguous_layout())
+
+
+def dg_get_sf_leading_dim(m):
+    return int(_lib.dg_get_sf_leading_dim(int(m)))
+
+
+def dg_get_last_error_string():
+    return _lib.dg_get_last_error_string().decode()
+
+
+def dg_describe_config(layout, m, n, k, num_groups=1, num_cus=256):
+    buf = ctypes.create_string_buffer(256)
+    _check("dg_describe_config", _lib.dg_describe_config(layout, m, n, k, num_groups, num_cus, buf, 256))
+    return buf.value.decode()
+
+
+def raw():
+    """The loaded ctypes library (for calling entry points with raw pointers)."""
+    return _lib

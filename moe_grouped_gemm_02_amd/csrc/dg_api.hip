@@ -1,0 +1,255 @@
+// C ABI of libdg: argument validation, error reporting, CU-count control and
+// dispatch to the gfx950 kernels.  Every check that can be made on the host
+// is made before anything is enqueued; nothing here allocates device memory
+// or synchronises the host.
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "dg.h"
+#include "dg_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+std::atomic<int> g_num_cus_override{0};
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return DG_SUCCESS;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int env_num_cus() {
+  const char* s = getenv("DG_NUM_CUS");
+  if (!s || !*s) return 0;
+  const int v = atoi(s);
+  return v > 0 ? v : 0;
+}
+
+// CU count the persistent schedule is sized to; negative on failure.
+int resolve_num_cus() {
+  const int forced = g_num_cus_override.load();
+  if (forced > 0) return forced;
+  const int env = env_num_cus();
+  if (env > 0) return env;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DG_ERR_HIP;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return DG_ERR_HIP;
+  return cus;
+}
+
+bool debug_enabled() {
+  const char* s = getenv("DG_DEBUG");
+  return s && *s && strcmp(s, "0") != 0;
+}
+
+const char* layout_name(int layout) {
+  return layout == dg::kDense ? "dense" : (layout == dg::kContiguous ? "contiguous" : "masked");
+}
+
+// Shared checks for the three GEMM entry points.  rows = the rows of the
+// layout's row space (M, M_total or M_max).
+int check_gemm_common(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                      const uint16_t* d, int rows, int n, int k, int64_t lda, int64_t ldb,
+                      int64_t ldd, int64_t ld_sfa) {
+  if (rows < 0 || n < 0 || k < 0) return fail(DG_ERR_INVALID_VALUE, "negative dimension (m=%d n=%d k=%d)", rows, n, k);
+  if (k % 128 != 0) return fail(DG_ERR_UNSUPPORTED_SHAPE, "k=%d is not a multiple of 128", k);
+  // With k == 0 nothing of A, B or the scales is read, so only d must be valid.
+  if (!d || (k > 0 && (!a || !sfa || !b || !sfb)))
+    return fail(DG_ERR_INVALID_VALUE, "null pointer argument");
+  if (!aligned16(a) || !aligned16(b) || !aligned16(d) || !aligned16(sfa) || !aligned16(sfb))
+    return fail(DG_ERR_MISALIGNED, "a, b, d, sfa and sfb must be 16-byte aligned");
+  if (lda < k || ldb < k) return fail(DG_ERR_INVALID_VALUE, "lda/ldb smaller than k");
+  if (ldd < n) return fail(DG_ERR_INVALID_VALUE, "ldd smaller than n");
+  if (lda % 16 || ldb % 16) return fail(DG_ERR_MISALIGNED, "lda and ldb must be multiples of 16 bytes");
+  if (ldd % 8) return fail(DG_ERR_MISALIGNED, "ldd must be a multiple of 8 elements");
+  if (ld_sfa < rows || ld_sfa < 4) return fail(DG_ERR_INVALID_VALUE, "ld_sfa=%lld smaller than rows (%d) or 4", (long long)ld_sfa, rows);
+  if (ld_sfa % 4) return fail(DG_ERR_MISALIGNED, "ld_sfa must be a multiple of 4");
+  const int64_t big = (int64_t)1 << 31;
+  if ((int64_t)rows * lda >= big * 8 || (int64_t)n * ldb >= big * 8)
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "operand too large");
+  return DG_SUCCESS;
+}
+
+int check_workspace(const dg::GemmConfig& cfg, int layout, int rows, int n, int groups,
+                    void* ws, size_t ws_bytes) {
+  const size_t need = dg::workspace_bytes_for(cfg, layout, rows, n, groups);
+  if (need == 0) return DG_SUCCESS;
+  if (!ws || ws_bytes < need)
+    return fail(DG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if (!aligned16(ws)) return fail(DG_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  return DG_SUCCESS;
+}
+
+int run_gemm(int layout, dg::GemmParams& p, int rows, int groups, void* ws, size_t ws_bytes,
+             void* stream) {
+  const int cus = resolve_num_cus();
+  if (cus < 0) return fail(DG_ERR_HIP, "cannot query the device's compute-unit count");
+  const dg::GemmConfig cfg = dg::choose_config(layout, rows, p.n, p.k, groups, cus);
+  int st = check_workspace(cfg, layout, rows, p.n, groups, ws, ws_bytes);
+  if (st != DG_SUCCESS) return st;
+  p.workspace = static_cast<float*>(ws);
+  p.counters = nullptr;
+  if (debug_enabled())
+    fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d: bm=%d bn=%d split_k=%d grid=%d tiles=%d variant=%d cus=%d\n",
+            layout_name(layout), rows, p.n, p.k, groups, cfg.bm, cfg.bn, cfg.split_k, cfg.grid,
+            cfg.tiles, cfg.variant, cus);
+  const hipError_t e = dg::launch_gemm(layout, p, cfg, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "GEMM launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
+                   int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_gemm_common(a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa);
+  if (st != DG_SUCCESS) return st;
+  if (m == 0 || n == 0) return ok();
+  dg::GemmParams p{};
+  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d;
+  p.m = m; p.n = n; p.k = k; p.num_groups = 1;
+  p.lda = lda; p.ldb = ldb; p.ldd = ldd; p.ld_sfa = ld_sfa;
+  return run_gemm(dg::kDense, p, m, 1, workspace, workspace_bytes, stream);
+}
+
+int dg_grouped_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
+                          const float* sfb, uint16_t* d, const int32_t* m_indices,
+                          int m_total, int n, int k, int num_groups, int64_t ld_sfa,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_groups < 1) return fail(DG_ERR_INVALID_VALUE, "num_groups must be >= 1");
+  int st = check_gemm_common(a, sfa, b, sfb, d, m_total, n, k, k, k, n, ld_sfa);
+  if (st != DG_SUCCESS) return st;
+  if (!m_indices) return fail(DG_ERR_INVALID_VALUE, "null m_indices");
+  if (m_total % 128) return fail(DG_ERR_UNSUPPORTED_SHAPE, "m_total=%d is not a multiple of 128", m_total);
+  if (n % 8) return fail(DG_ERR_MISALIGNED, "n must be a multiple of 8 (rows of d are packed)");
+  if (m_total == 0 || n == 0) return ok();
+  dg::GemmParams p{};
+  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.m_indices = m_indices;
+  p.m = m_total; p.n = n; p.k = k; p.num_groups = num_groups;
+  p.lda = k; p.ldb = k; p.ldd = n; p.ld_sfa = ld_sfa;
+  p.b_gstride = (int64_t)n * k;
+  p.sfb_gstride = (int64_t)((n + 127) / 128) * (k / 128);
+  return run_gemm(dg::kContiguous, p, m_total, num_groups, workspace, workspace_bytes, stream);
+}
+
+int dg_grouped_masked(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                      uint16_t* d, const int32_t* masked_m, int num_groups, int m_max, int n,
+                      int k, int expected_m, int64_t ld_sfa, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (num_groups < 1) return fail(DG_ERR_INVALID_VALUE, "num_groups must be >= 1");
+  if (expected_m < 0) return fail(DG_ERR_INVALID_VALUE, "expected_m must be >= 0");
+  int st = check_gemm_common(a, sfa, b, sfb, d, m_max, n, k, k, k, n, ld_sfa);
+  if (st != DG_SUCCESS) return st;
+  if (!masked_m) return fail(DG_ERR_INVALID_VALUE, "null masked_m");
+  if (n % 8) return fail(DG_ERR_MISALIGNED, "n must be a multiple of 8 (rows of d are packed)");
+  if (num_groups > 65535) return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many groups");
+  if (m_max == 0 || n == 0) return ok();
+  dg::GemmParams p{};
+  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.masked_m = masked_m;
+  p.m = m_max; p.n = n; p.k = k; p.num_groups = num_groups;
+  p.lda = k; p.ldb = k; p.ldd = n; p.ld_sfa = ld_sfa;
+  p.a_gstride = (int64_t)m_max * k;
+  p.sfa_gstride = (int64_t)(k / 128) * ld_sfa;
+  p.b_gstride = (int64_t)n * k;
+  p.sfb_gstride = (int64_t)((n + 127) / 128) * (k / 128);
+  p.d_gstride = (int64_t)m_max * n;
+  return run_gemm(dg::kMasked, p, m_max, num_groups, workspace, workspace_bytes, stream);
+}
+
+int dg_quant_1x128(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
+                   int64_t ld_sf, int num_groups, void* stream) {
+  if (rows < 0 || cols < 0 || num_groups < 1) return fail(DG_ERR_INVALID_VALUE, "bad sizes (rows=%d cols=%d groups=%d)", rows, cols, num_groups);
+  if (cols % 128) return fail(DG_ERR_UNSUPPORTED_SHAPE, "cols=%d is not a multiple of 128", cols);
+  if (ld_sf < rows) return fail(DG_ERR_INVALID_VALUE, "ld_sf smaller than rows");
+  if (ld_sf % 4) return fail(DG_ERR_MISALIGNED, "ld_sf must be a multiple of 4");
+  if (!x || !q || !sf) return fail(DG_ERR_INVALID_VALUE, "null pointer argument");
+  if (!aligned16(x) || !aligned16(q) || !aligned16(sf)) return fail(DG_ERR_MISALIGNED, "x, q and sf must be 16-byte aligned");
+  if (cols == 0 || ld_sf == 0) return ok();
+  const hipError_t e = dg::launch_quant_1x128(x, q, sf, rows, cols, ld_sf, num_groups,
+                                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "quant_1x128 launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int dg_quant_128x128(const uint16_t* w, uint8_t* q, float* sf, int rows, int cols,
+                     int num_groups, void* stream) {
+  if (rows < 0 || cols < 0 || num_groups < 1) return fail(DG_ERR_INVALID_VALUE, "bad sizes (rows=%d cols=%d groups=%d)", rows, cols, num_groups);
+  if (cols % 128) return fail(DG_ERR_UNSUPPORTED_SHAPE, "cols=%d is not a multiple of 128", cols);
+  if (!w || !q || !sf) return fail(DG_ERR_INVALID_VALUE, "null pointer argument");
+  if (!aligned16(w) || !aligned16(q) || !aligned16(sf)) return fail(DG_ERR_MISALIGNED, "w, q and sf must be 16-byte aligned");
+  if (num_groups > 65535 || (rows + 127) / 128 > 65535) return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many blocks");
+  if (rows == 0 || cols == 0) return ok();
+  const hipError_t e = dg::launch_quant_128x128(w, q, sf, rows, cols, num_groups,
+                                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "quant_128x128 launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t dg_get_workspace_size(int m, int n, int k, int num_groups) {
+  if (m <= 0 || n <= 0 || k <= 0 || num_groups < 1) return 0;
+  int cus = resolve_num_cus();
+  if (cus < 0) cus = 256;
+  size_t worst = 0;
+  for (int layout = dg::kDense; layout <= dg::kMasked; ++layout) {
+    const dg::GemmConfig c = dg::choose_config(layout, m, n, k, num_groups, cus);
+    const size_t need = dg::workspace_bytes_for(c, layout, m, n, num_groups);
+    if (need > worst) worst = need;
+  }
+  return worst;
+}
+
+int dg_get_num_cus(void) {
+  const int v = resolve_num_cus();
+  if (v < 0) return fail(DG_ERR_HIP, "cannot query the device's compute-unit count");
+  return v;
+}
+
+int dg_set_num_cus(int num_cus) {
+  if (num_cus < 0) return fail(DG_ERR_INVALID_VALUE, "num_cus must be >= 0");
+  g_num_cus_override.store(num_cus);
+  return ok();
+}
+
+int dg_get_m_alignment_for_contiguous_layout(void) { return 128; }
+
+int64_t dg_get_sf_leading_dim(int m) {
+  if (m < 0) return -1;
+  return ((int64_t)m + 3) / 4 * 4;
+}
+
+const char* dg_get_last_error_string(void) { return g_last_error; }
+
+int dg_describe_config(int layout, int m, int n, int k, int num_groups, int num_cus, char* buf,
+                       size_t len) {
+  if (layout < dg::kDense || layout > dg::kMasked || m < 0 || n < 0 || k < 0 ||
+      num_groups < 1 || num_cus < 1 || !buf || len == 0)
+    return fail(DG_ERR_INVALID_VALUE, "bad arguments to dg_describe_config");
+  const dg::GemmConfig c = dg::choose_config(layout, m, n, k, num_groups, num_cus);
+  snprintf(buf, len, "layout=%s bm=%d bn=%d split_k=%d grid=%d tiles=%d variant=%d workspace=%zu",
+           layout_name(layout), c.bm, c.bn, c.split_k, c.grid, c.tiles, c.variant,
+           dg::workspace_bytes_for(c, layout, m, n, num_groups));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Internal host/device interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+enum Layout : int { kDense = 0, kContiguous = 1, kMasked = 2 };
+
+// Everything a GEMM kernel needs; group strides are in elements.
+struct GemmParams {
+  const uint8_t* a;
+  const float* sfa;
+  const uint8_t* b;
+  const float* sfb;
+  uint16_t* d;
+  const int32_t* m_indices;  // contiguous layout only
+  const int32_t* masked_m;   // masked layout only
+  float* workspace;          // split-K partials (fp32), may be null
+  int* counters;             // split-K arrival counters, may be null
+  int m;                     // dense: M; contiguous: M_total; masked: M_max
+  int n;
+  int k;
+  int num_groups;
+  int64_t lda, ldb, ldd, ld_sfa;
+  int64_t a_gstride, sfa_gstride, b_gstride, sfb_gstride, d_gstride;
+};
+
+// Tile configuration chosen on the host (deterministically, from the shape).
+struct GemmConfig {
+  int bm;
+  int bn;
+  int split_k;   // number of K ranges per output tile (1 = none)
+  int grid;      // workgroups launched
+  int tiles;     // output tiles (per split) over all groups
+  int variant;   // kernel family index
+};
+
+GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cus);
+size_t workspace_bytes_for(const GemmConfig& cfg, int layout, int m, int n, int groups);
+
+hipError_t launch_gemm(int layout, const GemmParams& p, const GemmConfig& cfg,
+                       hipStream_t stream);
+hipError_t launch_quant_1x128(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
+                              int64_t ld_sf, int groups, hipStream_t stream);
+hipError_t launch_quant_128x128(const uint16_t* w, uint8_t* q, float* sf, int rows, int cols,
+                                int groups, hipStream_t stream);
+
+}  // namespace dg

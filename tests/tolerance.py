@@ -7,9 +7,17 @@ rows the method writes.  A GPU result c passes when
 bf16 rounding of the exact result alone gives a relative L2 error of about
 1.7e-3 on N(0,1) inputs, so the rule leaves room for fp32 accumulation in any
 order and nothing more.
+
+On very small outputs the correctly rounded bf16 result alone can exceed the
+2e-3 bound (a 1x16 output measured 2.28e-3), and no bf16 output can do
+better than correct rounding; there the rel-L2 bound is 1.1 times the rel-L2
+of the correctly rounded oracle result.  For realistic sizes that figure is
+about 1.7e-3 and the bound stays 2e-3.
 """
 
 import numpy as np
+
+from oracle import bf16
 
 REL_L2 = 2e-3
 ABS_RMS = 1e-2
@@ -30,6 +38,8 @@ def check(c, ref, what=""):
     bound = ABS_RMS * rms + REL_ELT * np.abs(ref)
     worst = float(np.max(diff / np.where(bound > 0, bound, 1.0)))
     bad = int(np.count_nonzero(diff > bound))
-    assert rel_l2 <= REL_L2 or norm == 0, f"{what}: rel-L2 {rel_l2:.3e} > {REL_L2}"
+    rounded = np.linalg.norm(bf16.round_f64(ref) - ref) / norm if norm > 0 else 0.0
+    limit = max(REL_L2, 1.1 * rounded)
+    assert rel_l2 <= limit or norm == 0, f"{what}: rel-L2 {rel_l2:.3e} > {limit:.3e}"
     assert bad == 0, f"{what}: {bad} elements outside the per-element bound (worst ratio {worst:.3f})"
     return {"rel_l2": float(rel_l2), "worst": worst}
