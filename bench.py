@@ -132,7 +132,7 @@ class Prepared:
         else:
             self.m_valid = wl.m
         ws = dg.dg_get_workspace_size(self.m_rows, n, k, g)
-        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
+        self.ws = torch.zeros(ws, dtype=torch.uint8, device=dev) if ws else None
         self.flops = algorithmic_flops(self.m_valid, n, k)
         self.bytes = algorithmic_bytes(self.m_valid, n, k, g)
         self.sf_bytes = scale_bytes(self.m_valid, n, k, g)
@@ -156,6 +156,27 @@ class Prepared:
 
 # ------------------------------------------------------------------ timing --
 
+def _enqueue_ahead(torch, enqueue_fn):
+    """Run enqueue_fn while the GPU is held by a sleep kernel.
+
+    The host then queues all the timed work before the GPU starts on it, so
+    kernel timings are device time, not host launch rate.  Returns the host
+    seconds spent enqueueing and whether the sleep outlasted them.
+    """
+    sleep_cycles = int(2e8)
+    torch.cuda.synchronize()
+    probe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    probe[0].record()
+    torch.cuda._sleep(sleep_cycles)
+    probe[1].record()
+    t0 = time.perf_counter()
+    enqueue_fn()
+    host_s = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    sleep_s = probe[0].elapsed_time(probe[1]) * 1e-3
+    return host_s, sleep_s > host_s
+
+
 def time_steps(dg, torch, preps, steps, warmup):
     """Time `steps` whole steps; GEMM launches are bracketed by events too."""
     stream = torch.cuda.current_stream()
@@ -166,31 +187,37 @@ def time_steps(dg, torch, preps, steps, warmup):
     torch.cuda.synchronize()
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in preps] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for s in range(steps):
-        for i, p in enumerate(preps):
-            p.quant(dg)
-            ev[s][i][0].record(stream)
-            p.gemm(dg, warmup + s)
-            ev[s][i][1].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
+
+    def enqueue():
+        start.record(stream)
+        for s in range(steps):
+            for i, p in enumerate(preps):
+                p.quant(dg)
+                ev[s][i][0].record(stream)
+                p.gemm(dg, warmup + s)
+                ev[s][i][1].record(stream)
+        end.record(stream)
+
+    host_s, ahead = _enqueue_ahead(torch, enqueue)
+    if not ahead:
+        print(f"warning: host enqueue ({host_s * 1e3:.1f} ms) outlasted the GPU sleep; timings include host gaps",
+              file=sys.stderr)
     total_ms = start.elapsed_time(end)
     gemm_ms = np.array([[a.elapsed_time(b) for (a, b) in row] for row in ev])  # [steps][shapes]
     return total_ms, gemm_ms
 
 
 def time_quant(dg, torch, p, reps=20):
-    stream = torch.cuda.current_stream()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     p.quant(dg)
-    torch.cuda.synchronize()
-    s.record(stream)
-    for _ in range(reps):
-        p.quant(dg)
-    e.record(stream)
-    torch.cuda.synchronize()
+
+    def enqueue():
+        s.record()
+        for _ in range(reps):
+            p.quant(dg)
+        e.record()
+
+    _enqueue_ahead(torch, enqueue)
     return s.elapsed_time(e) / reps
 
 
@@ -199,42 +226,45 @@ def time_quant(dg, torch, p, reps=20):
 def cpu_baseline(wls, target_s):
     """The oracle, single-threaded, on a bounded sample of the workload.
 
-    Sample: for each shape, the full M rows of A against the first 512 columns
-    of B (four 128-row weight blocks), quantising both from bf16 like the GPU
-    step does (the weight quantisation is excluded from the GPU step, so it is
-    excluded here too).  Shapes are visited in order until about target_s
-    seconds of work are done.  Rate = sample flops / oracle seconds.
+    Sample: for each shape, all M rows of A (at most 256) against the first
+    1024 columns of B (eight 128-row weight blocks).  The activations are
+    quantised inside the timed region, as in the GPU step; the weights are
+    quantised before it, as in the GPU step.  The shapes are visited in turn,
+    repeatedly, until about target_s seconds of oracle work are done.
+    Rate = sample flops / oracle seconds.
     """
     import synth
     from oracle import gemm, quant
     from threadpoolctl import threadpool_limits
 
+    samples = []
+    for wl in wls:
+        m = wl.m if wl.layout == "dense" else min(wl.m, 256)
+        ncols = min(wl.n, 1024)
+        xa = synth.bf16_normal((m, wl.k), wl.seed_a)
+        qb, sfb = quant.quant_128x128(synth.bf16_normal((ncols, wl.k), wl.seed_b))
+        samples.append((wl, m, ncols, xa, qb, sfb))
     flops = 0.0
     secs = 0.0
-    done = []
+    runs = 0
     with threadpool_limits(limits=1):
-        for wl in wls:
-            m = wl.m if wl.layout == "dense" else min(wl.m, 256)
-            ncols = min(wl.n, 512)
-            xa = synth.bf16_normal((m, wl.k), wl.seed_a)
-            xb = synth.bf16_normal((ncols, wl.k), wl.seed_b)
-            qb, sfb = quant.quant_128x128(xb)
+        while secs < target_s and runs < 20 * len(samples):
+            wl, m, ncols, xa, qb, sfb = samples[runs % len(samples)]
             t0 = time.perf_counter()
             qa, sfa = quant.quant_1x128(xa)
             gemm.gemm_nt_ref(qa, sfa, qb, sfb)
             secs += time.perf_counter() - t0
             flops += algorithmic_flops(m, ncols, wl.k)
-            done.append(f"{wl.name}[:{m}, :{ncols}]")
-            if secs >= target_s:
-                break
+            runs += 1
+    names = ", ".join(f"{wl.name}[:{m}, :{nc}]" for wl, m, nc, *_ in samples)
     return {
         "value": flops / secs / 1e12,
         "unit": "TFLOPS",
         "cores": 1,
         "kind": "oracle",
-        "sample": "single-threaded numpy oracle (quantise A per 1x128 + fp64 blockwise GEMM) on "
-                  + ", ".join(done) + f"; {secs:.1f} s of CPU work",
-        "cpu_model": platform.processor() or _cpu_model(),
+        "sample": f"single-threaded numpy oracle (quantise A per 1x128 + fp64 blockwise GEMM), {runs} runs "
+                  f"cycling over {names}; {secs:.1f} s of CPU work",
+        "cpu_model": _cpu_model(),
         "host_cores": os.cpu_count(),
     }
 

@@ -67,8 +67,8 @@ typedef enum {
  *   sfb [ceil(n/128)][k/128] fp32 (the last row block may be partial)
  *   d   [m][ldd]  bf16 output; only columns < n of rows < m are written
  *   workspace: device scratch of at least dg_get_workspace_size(m, n, k, 1)
- *       bytes (may be NULL when that size is 0); contents need not be
- *       initialised and are clobbered.
+ *       bytes (may be NULL when that size is 0); zero-filled before its first
+ *       use, see dg_get_workspace_size.
  */
 int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
                    uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
@@ -149,7 +149,11 @@ int dg_quant_128x128(const uint16_t* w, uint8_t* q, float* sf, int rows, int col
 /* -------------------------------------------------------------- utilities -- */
 
 /* Workspace bytes a GEMM of this shape needs (0 when it needs none).  For the
- * masked layout pass m = m_max; for contiguous pass m = m_total. */
+ * masked layout pass m = m_max; for contiguous pass m = m_total.
+ * The workspace holds split-K partial sums and per-tile arrival counters.  It
+ * must be zero-filled once before its first use; every call leaves it ready
+ * for the next one (counters back at zero), so it can be reused without
+ * clearing.  Calls that run at the same time must not share a workspace. */
 size_t dg_get_workspace_size(int m, int n, int k, int num_groups);
 
 /* Number of compute units the persistent kernels are sized to (set_num_sms /

@@ -82,9 +82,10 @@ int check_gemm_common(const uint8_t* a, const float* sfa, const uint8_t* b, cons
   if (ldd % 8) return fail(DG_ERR_MISALIGNED, "ldd must be a multiple of 8 elements");
   if (ld_sfa < rows || ld_sfa < 4) return fail(DG_ERR_INVALID_VALUE, "ld_sfa=%lld smaller than rows (%d) or 4", (long long)ld_sfa, rows);
   if (ld_sfa % 4) return fail(DG_ERR_MISALIGNED, "ld_sfa must be a multiple of 4");
-  const int64_t big = (int64_t)1 << 31;
-  if ((int64_t)rows * lda >= big * 8 || (int64_t)n * ldb >= big * 8)
-    return fail(DG_ERR_UNSUPPORTED_SHAPE, "operand too large");
+  // The kernels address each operand (per group) with 32-bit byte offsets.
+  const int64_t lim = (int64_t)1 << 32;
+  if ((int64_t)rows * lda >= lim || (int64_t)n * ldb >= lim || (int64_t)(k / 128) * ld_sfa * 4 >= lim)
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "operand of 4 GiB or more (per group)");
   return DG_SUCCESS;
 }
 

@@ -7,21 +7,37 @@
 // weight scale) and add it into an fp32 accumulator ("promotion" every
 // N_C = 128).  Output bf16.
 //
-// gfx950 mapping: one v_mfma_f32_16x16x128_f8f6f4 covers exactly one 128-deep
-// scale slice of a 16x16 output fragment, so the partial product never mixes
-// two slices and needs no chained accumulation: P = mfma(a, b, 0), then
-// acc += P * (sa * sb) on the VALU, per lane for its 4 rows x 1 column.
+// gfx950 mapping
+// * One v_mfma_f32_16x16x128_f8f6f4 covers exactly one 128-deep scale slice of
+//   a 16x16 output fragment, so a partial product never mixes two slices:
+//   P = mfma(a, b, 0), then acc += P * (sa * sb) on the VALU, per lane for its
+//   4 rows x 1 column.
+// * Fragment layouts (64-wide wavefronts).  Operand: lane l holds 32 bytes of
+//   K for row (l % 16), lane group l / 16 selects which 32 bytes; A and B use
+//   the same K assignment, so the contraction is the full 128-term dot product
+//   whatever order the matrix core visits the bytes in.  Result: lane l holds
+//   column (l % 16), rows 4 * (l / 16) + i, i = 0..3.
+// * Operands are staged HBM -> LDS with global_load_lds_dwordx4 (no register
+//   staging), STAGES deep, one barrier per K slice.  A stage holds the A tile
+//   [BM][128], the B tile [BN][128] and the BM activation scales of the slice.
+//   Tiles are row-major with 128-byte rows and the 16-byte chunk c of row r
+//   stored at position c ^ (r % 8), so 8 lanes reading 8 consecutive rows at
+//   one K offset touch 8 distinct 16-byte bank groups.
+// * Persistent workgroups (grid sized to the CU count) walk the work units;
+//   units that run at the same time on one XCD (workgroup id mod 8) are given
+//   neighbouring tiles so they share A and B lines in that XCD's L2.
+// * Split-K (for shapes with fewer tiles than CUs): each unit computes a K
+//   range of one tile and writes an fp32 partial; the last unit of a tile to
+//   finish (arrival counter) sums the partials in split order - a fixed order,
+//   so results are bit-identical run to run - and stores bf16.  The splits of
+//   a tile are placed on one XCD so the partials stay in its L2.
 //
-// Fragment layouts (64-wide wavefronts):
-//   A/B operand: lane l holds 32 bytes of K for row (l % 16); lane group
-//   l / 16 selects which 32 bytes.  A and B use the same K assignment, so the
-//   contraction over the slice is the full 128-term dot product whatever order
-//   the matrix core visits the bytes in.
-//   Result: lane l holds column (l % 16), rows 4 * (l / 16) + i, i = 0..3.
-//
-// LDS tiles are row-major with 128-byte rows; the 16-byte chunk c of row r is
-// stored at chunk position c ^ (r % 8), so that the 16 lanes reading 16
-// consecutive rows at the same K offset hit distinct banks.
+// The unaligned tile widths (BN not a power of two) follow the pages' point
+// that power-of-two blocks can leave SMs idle (project introduction,
+// Optimisations, "unaligned block sizes").
+
+#include <stdlib.h>
+#include <string.h>
 
 #include "dg_device.h"
 #include "dg_internal.h"
@@ -30,7 +46,42 @@ namespace dg {
 
 namespace {
 
-constexpr int kThreads = 256;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16-byte asynchronous copy global -> LDS.  The LDS destination of lane l is
+// m0 + 16 * l, so one instruction fills 1 KB of LDS.  Written as inline asm so
+// that the compiler does not add a conservative vmcnt(0) before every LDS read
+// (it cannot tell which stage a DMA targets); the pipeline waits explicitly.
+__device__ __forceinline__ void dma16(uint32_t lds, const void* base, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(off), "s"(base)
+               : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector memory operations are in flight,
+// then barrier.  The "memory" clobber keeps the compiler from moving LDS or
+// global accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
+// Pointers that are the same for the whole wave, kept in SGPRs (the DMA takes
+// its base address from an SGPR pair).
+template <class P>
+__device__ __forceinline__ P* uniform_ptr(P* ptr) {
+  const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
+}
 
 __device__ __forceinline__ v8i make_v8i(uint4 lo, uint4 hi) {
   v8i r;
@@ -42,226 +93,429 @@ __device__ __forceinline__ v8i make_v8i(uint4 lo, uint4 hi) {
 __device__ __forceinline__ v4f mfma_fp8_slice(const v8i& a, const v8i& b) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   // Format codes 0/0 = e4m3 for both operands; no block scale (the scales here
-  // are arbitrary fp32 values, applied on the VALU below).
+  // are arbitrary fp32 values, applied on the VALU).
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
-// Basic tiled kernel: one BM x BN output tile per workgroup of four waves
-// (2 x 2), each wave owning a (BM/2) x (BN/2) sub-tile of 16x16 fragments.
-// HBM -> registers -> LDS double buffering, one barrier per K slice.
-template <int BM, int BN, int LAYOUT>
-__global__ __launch_bounds__(kThreads) void gemm_tile_kernel(GemmParams p) {
-  constexpr int kWavesN = 2;
-  constexpr int TM = BM / 2, TN = BN / kWavesN;
-  constexpr int FM = TM / 16, FN = TN / 16;
-  constexpr int LA = BM * 8 / kThreads;  // 16-byte chunks per thread per slice
-  constexpr int LB = BN * 8 / kThreads;
-  static_assert(FM >= 1 && FN >= 1 && LA >= 1 && LB >= 1, "tile too small");
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+  static constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 fragments per wave
+  static constexpr int kAInstr = BM / 8;            // 1 KB DMA instructions per slice
+  static constexpr int kBInstr = BN / 8;
+  static constexpr int kSInstr = (BM / 4 + 63) / 64; // fp32 activation scales
+  static constexpr int kInstr = kAInstr + kBInstr + kSInstr;
+  static constexpr int kLPW = (kInstr + kWaves - 1) / kWaves;  // DMA per wave per stage
+  static constexpr int kStageBytes = kLPW * kWaves * 1024;
+  static constexpr int kBOff = BM * 128;
+  static constexpr int kSOff = (BM + BN) * 128;
+  static constexpr bool kOneSB = (128 % TN) == 0;   // wave columns inside one 128-block
+  static_assert(TM % 16 == 0 && TN % 16 == 0 && BM % 8 == 0 && BN % 8 == 0, "bad tile");
+  static_assert(STAGES >= 2, "need two stages");
+  static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS overflow");
+};
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * kBlockK];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * kBlockK];
-  __shared__ int row_group[BM];
-  __shared__ int wave_group[kThreads / 64];
+// Decode a linear work-unit index into a tile.  XCD-aware: workgroup w runs on
+// XCD w % 8, so within a round the units of one XCD (w = x, x+8, ...) are
+// remapped onto consecutive tile indices; tiles are then rastered in groups of
+// `group_m` M-tiles so that consecutive indices share rows of A and walk N.
+__device__ __forceinline__ int xcd_remap(int u, int grid, int units) {
+  const int round_base = (u / grid) * grid;
+  if (round_base + grid > units || (grid & 7)) return u;  // last partial round: identity
+  const int w = u - round_base;
+  return round_base + (w & 7) * (grid >> 3) + (w >> 3);
+}
+
+__device__ __forceinline__ void raster(int t, int m_tiles, int n_tiles, int group_m, int& mt,
+                                       int& nt) {
+  const int per_group = group_m * n_tiles;
+  const int grp = t / per_group;
+  const int first = grp * group_m;
+  const int gsize = min(group_m, m_tiles - first);
+  const int r = t - grp * per_group;
+  mt = first + r % gsize;
+  nt = r / gsize;
+}
+
+__device__ __forceinline__ int clamp_rows(int v, int hi) { return v < 0 ? 0 : (v > hi ? hi : v); }
+
+template <class T, int LAYOUT, bool SPLIT>
+__global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedule s) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::STAGES * T::kStageBytes];
+  __shared__ int last_flag;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / kWavesN, wn = wave % kWavesN;
-  const int n0 = blockIdx.x * BN;
-  const int m0 = blockIdx.y * BM;
-  int g = blockIdx.z;
-
-  const uint8_t* A = p.a;
-  const float* SA = p.sfa;
-  uint16_t* D = p.d;
-  int rows_valid = p.m;
-
-  if (LAYOUT == kMasked) {
-    int mm = p.masked_m[g];
-    mm = mm < 0 ? 0 : (mm > p.m ? p.m : mm);
-    if (m0 >= mm) return;  // uniform across the workgroup
-    rows_valid = mm;
-    A += (int64_t)g * p.a_gstride;
-    SA += (int64_t)g * p.sfa_gstride;
-    D += (int64_t)g * p.d_gstride;
-  } else if (LAYOUT == kContiguous) {
-    int id = -1;
-    if (tid < BM) {
-      id = p.m_indices[m0 + tid];
-      if (id < 0 || id >= p.num_groups) id = -1;
-      row_group[tid] = id;
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) id = max(id, __shfl_xor(id, off, 64));
-    if (lane == 0) wave_group[wave] = id;
-    __syncthreads();
-    g = wave_group[0];
-#pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) g = max(g, wave_group[w]);
-    if (g < 0) return;  // an all-padding block: nothing to write
-  }
-  const uint8_t* B = p.b + (int64_t)g * p.b_gstride;
-  const float* SB = p.sfb + (int64_t)g * p.sfb_gstride;
-
-  const int nkb = p.k / kBlockK;
-  const int n_blocks = (p.n + kBlockK - 1) / kBlockK;
-
-  // Global -> register staging: chunk (tid + 256 i) is row (tid / 8 + 32 i),
-  // 16-byte column (tid % 8) of the slice.
-  const int ch = tid & 7;
-  uint4 ra[LA], rb[LB];
-  auto load_slice = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      const int gr = min(m0 + r, rows_valid - 1);
-      ra[i] = *reinterpret_cast<const uint4*>(A + (int64_t)gr * p.lda + kb * kBlockK + ch * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < LB; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      const int gn = min(n0 + r, p.n - 1);
-      rb[i] = *reinterpret_cast<const uint4*>(B + (int64_t)gn * p.ldb + kb * kBlockK + ch * 16);
-    }
-  };
-  auto store_slice = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      *reinterpret_cast<uint4*>(&lds_a[buf][r * kBlockK + ((ch ^ (r & 7)) << 4)]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < LB; ++i) {
-      const int r = (tid >> 3) + 32 * i;
-      *reinterpret_cast<uint4*>(&lds_b[buf][r * kBlockK + ((ch ^ (r & 7)) << 4)]) = rb[i];
-    }
-  };
-
-  v4f acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-  const int fr = lane & 15;        // fragment row (A) / column (B) of this lane
-  const int kg = lane >> 4;        // which 32 bytes of the slice
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / T::WN, wn = wave % T::WN;
+  const int fr = lane & 15;  // fragment row (A) / column (B) of this lane
+  const int kg = lane >> 4;  // which 32 bytes of the slice
   const int c0 = (2 * kg) ^ (fr & 7), c1 = (2 * kg + 1) ^ (fr & 7);
+  const int nkb_total = p.k / kBlockK;
+  const int n_blocks = (p.n + kBlockK - 1) / kBlockK;
+  const uint32_t smem_base = lds_addr(smem);
 
-  if (nkb > 0) {
-    load_slice(0);
-    store_slice(0);
+  // Work units.  Masked: the number of valid M tiles is read on the device.
+  int m_tiles = s.m_tiles;
+  if (LAYOUT == kMasked) {
+    m_tiles = 0;
+    for (int g = 0; g < p.num_groups; ++g)
+      m_tiles += (clamp_rows(p.masked_m[g], p.m) + T::BM - 1) / T::BM;
   }
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) load_slice(kb + 1);
+  const int tiles = m_tiles * s.n_tiles;
+  const int units = SPLIT ? ((tiles + 7) / 8) * 8 * s.split_k : tiles;
 
-    // Scales of this slice: 4 consecutive rows per fragment row-block.
-    float sa[FM][4];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      int r4 = m0 + wm * TM + i * 16 + 4 * kg;
-      r4 = min(r4, (int)p.ld_sfa - 4);
-      const float4 s4 = *reinterpret_cast<const float4*>(SA + (int64_t)kb * p.ld_sfa + r4);
-      sa[i][0] = s4.x; sa[i][1] = s4.y; sa[i][2] = s4.z; sa[i][3] = s4.w;
+  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+    // ------------------------------------------------------------ schedule
+    int t, split = 0;
+    if (SPLIT) {
+      // Units are ordered so that the splits of one tile are 8 apart, i.e. on
+      // the same XCD: u = (tile / 8) * 8 * S + split * 8 + tile % 8.
+      const int blk = u / (8 * s.split_k);
+      const int r = u - blk * 8 * s.split_k;
+      split = r >> 3;
+      t = blk * 8 + (r & 7);
+      if (t >= tiles) continue;
+    } else {
+      t = xcd_remap(u, gridDim.x, units);
     }
-    float sb[FN];
+    int mt, nt;
+    raster(t, m_tiles, s.n_tiles, s.group_m, mt, nt);
+    int g = 0;
+    if (LAYOUT == kMasked) {
+      int before = 0;
+      for (g = 0; g < p.num_groups - 1; ++g) {
+        const int gt = (clamp_rows(p.masked_m[g], p.m) + T::BM - 1) / T::BM;
+        if (mt < before + gt) break;
+        before += gt;
+      }
+      mt -= before;
+    }
+    const int m0 = mt * T::BM;
+    const int n0 = nt * T::BN;
+    const int kb0 = split * s.kb_per_split;
+    const int kb1 = min(nkb_total, kb0 + s.kb_per_split);
+
+    int rows_valid = p.m;
+    const uint8_t* A = p.a;
+    const float* SA = p.sfa;
+    uint16_t* D = p.d;
+    if (LAYOUT == kMasked) {
+      rows_valid = clamp_rows(p.masked_m[g], p.m);
+      A += (int64_t)g * p.a_gstride;
+      SA += (int64_t)g * p.sfa_gstride;
+      D += (int64_t)g * p.d_gstride;
+    }
+    // Contiguous layout: the experts of the tile's 128-row halves.  A tile
+    // whose halves belong to two experts is computed once per expert.
+    int pass_group[2] = {0, -1};
+    int passes = 1;
+    if (LAYOUT == kContiguous) {
+      int gh[2] = {-1, -1};
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int cb = min((n0 + wn * TN + j * 16) >> 7, n_blocks - 1);
-      sb[j] = SB[cb * nkb + kb];
+      for (int h = 0; h < (T::BM + 127) / 128; ++h) {
+        int id = -1;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int row = m0 + h * 128 + lane * 2 + q;
+          if (row < p.m && row < m0 + T::BM) {
+            const int v = p.m_indices[row];
+            if (v >= 0 && v < p.num_groups) id = max(id, v);
+          }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) id = max(id, __shfl_xor(id, off, 64));
+        gh[h] = __builtin_amdgcn_readfirstlane(id);
+      }
+      passes = 0;
+      if (gh[0] >= 0) pass_group[passes++] = gh[0];
+      if (gh[1] >= 0 && gh[1] != gh[0]) pass_group[passes++] = gh[1];
     }
 
-    v8i af[FM], bf[FN];
+    A = uniform_ptr(A);
+    SA = uniform_ptr(SA);
+    for (int pass = 0; pass < passes; ++pass) {
+      if (LAYOUT == kContiguous) g = __builtin_amdgcn_readfirstlane(pass == 0 ? pass_group[0] : pass_group[1]);
+      const uint8_t* B = uniform_ptr(p.b + (int64_t)g * p.b_gstride);
+      const float* SB = uniform_ptr(p.sfb + (int64_t)g * p.sfb_gstride);
+      const int nkb = kb1 - kb0;
+
+      // Stage loader.  DMA instruction i of a stage fills LDS bytes
+      // [1024 i, 1024 i + 1024): instructions [0, BM/8) carry A rows,
+      // [BM/8, (BM+BN)/8) B rows, then the BM activation scales, then padding
+      // so that every wave issues exactly kLPW instructions per stage.
+      auto issue_stage = [&](int kb, int buf) {
+        const uint32_t stage_lds = smem_base + buf * T::kStageBytes;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const uint8_t* rowp = &lds_a[buf][(wm * TM + i * 16 + fr) * kBlockK];
-      af[i] = make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
-                       *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
-    }
+        for (int j = 0; j < T::kLPW; ++j) {
+          const int instr = j * T::kWaves + wave;  // wave-uniform
+          if (instr < T::kAInstr) {
+            const int q = instr * 64 + lane;
+            const int r = q >> 3, c = (q & 7) ^ (r & 7);
+            const int gr = min(m0 + r, rows_valid - 1);
+            dma16(stage_lds + instr * 1024, A, (uint32_t)gr * (uint32_t)p.lda + kb * 128 + c * 16);
+          } else if (instr < T::kAInstr + T::kBInstr) {
+            const int q = (instr - T::kAInstr) * 64 + lane;
+            const int r = q >> 3, c = (q & 7) ^ (r & 7);
+            const int gn = min(n0 + r, p.n - 1);
+            dma16(stage_lds + instr * 1024, B, (uint32_t)gn * (uint32_t)p.ldb + kb * 128 + c * 16);
+          } else if (instr < T::kAInstr + T::kBInstr + T::kSInstr) {
+            const int q = (instr - T::kAInstr - T::kBInstr) * 64 + lane;
+            const int r4 = min(m0 + 4 * q, (int)p.ld_sfa - 4);
+            dma16(stage_lds + instr * 1024, SA, (uint32_t)(kb * p.ld_sfa + r4) * 4u);
+          } else {
+            dma16(stage_lds + instr * 1024, A, 0u);  // padding
+          }
+        }
+      };
+
+      v4f acc[T::FM][T::FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const uint8_t* rowp = &lds_b[buf][(wn * TN + j * 16 + fr) * kBlockK];
-      bf[j] = make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
-                       *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
-    }
+      for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+        for (int j = 0; j < T::FN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+      lds_barrier();  // previous unit's readers are done with every buffer
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const v4f part = mfma_fp8_slice(af[i], bf[j]);
+      for (int st = 0; st < T::STAGES - 1; ++st)
+        if (st < nkb) issue_stage(kb0 + st, st);
+
+      for (int it = 0; it < nkb; ++it) {
+        if (it + T::STAGES - 2 < nkb) wait_vm_barrier<(T::STAGES - 2) * T::kLPW>();
+        else wait_vm_barrier<0>();
+        if (it + T::STAGES - 1 < nkb) issue_stage(kb0 + it + T::STAGES - 1, (it + T::STAGES - 1) % T::STAGES);
+
+        const int kb = kb0 + it;
+        const uint8_t* st = smem + (it % T::STAGES) * T::kStageBytes;
+        float sbw = 0.0f;
+        float sbv[T::FN];
+        if (T::kOneSB) {
+          const int cb = min((n0 + wn * T::TN) >> 7, n_blocks - 1);
+          sbw = SB[cb * nkb_total + kb];
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(part[e], sa[i][e] * sb[j], acc[i][j][e]);
+          for (int j = 0; j < T::FN; ++j) {
+            const int cb = min((n0 + wn * T::TN + j * 16) >> 7, n_blocks - 1);
+            sbv[j] = SB[cb * nkb_total + kb];
+          }
+        }
+        v8i bfrag[T::FN];
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+          const uint8_t* rowp = st + T::kBOff + (wn * T::TN + j * 16 + fr) * 128;
+          bfrag[j] = make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
+                              *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
+        }
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i) {
+          const uint8_t* rowp = st + (wm * T::TM + i * 16 + fr) * 128;
+          const v8i afrag = make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
+                                     *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
+          const float4 s4 = *reinterpret_cast<const float4*>(st + T::kSOff + (wm * T::TM + i * 16 + 4 * kg) * 4);
+          const float sa[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+          for (int j = 0; j < T::FN; ++j) {
+            const v4f part = mfma_fp8_slice(afrag, bfrag[j]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float sc = T::kOneSB ? sa[e] * sbw : sa[e] * sbv[j];
+              acc[i][j][e] = fmaf(part[e], sc, acc[i][j][e]);
+            }
+          }
+        }
       }
 
-    if (kb + 1 < nkb) store_slice(buf ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue: bf16 (RNE) stores of the rows this layout writes.
+      // ------------------------------------------------------- split-K fixup
+      if (SPLIT && s.split_k > 1) {
+        float4* ws = reinterpret_cast<float4*>(p.workspace);
+        const int fr_per = T::FM * T::FN;
+        float4* mine = ws + ((int64_t)(t * s.split_k + split) * fr_per) * T::kThreads;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int rl = wm * TM + i * 16 + 4 * kg + e;
-      const int row = m0 + rl;
-      bool ok;
-      if (LAYOUT == kContiguous) ok = row_group[rl] == g;
-      else ok = row < rows_valid;
-      if (!ok) continue;
+          for (int j = 0; j < T::FN; ++j)
+            mine[(i * T::FN + j) * T::kThreads + tid] = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) {
+          const int old = atomicAdd(&p.counters[t], 1);
+          last_flag = (old == s.split_k - 1);
+        }
+        __syncthreads();
+        if (!last_flag) continue;
+        __threadfence();
+        // Sum every split's partial, this unit's own included, in split order.
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * TN + j * 16 + fr;
-        if (col < p.n) D[(int64_t)row * p.ldd + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
+        for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < T::FN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int sp = 0; sp < s.split_k; ++sp) {
+          const float4* src = ws + ((int64_t)(t * s.split_k + sp) * fr_per) * T::kThreads;
+#pragma unroll
+          for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j)
+              acc[i][j] += *reinterpret_cast<const v4f*>(src + (i * T::FN + j) * T::kThreads + tid);
+        }
+        if (tid == 0) p.counters[t] = 0;  // ready for the next call
       }
+
+      // ------------------------------------------------------------ epilogue
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = m0 + wm * T::TM + i * 16 + 4 * kg + e;
+          bool ok = row < rows_valid && row < m0 + T::BM;
+          if (LAYOUT == kContiguous && ok) ok = p.m_indices[row] == g;
+          if (!ok) continue;
+          uint16_t* drow = D + (int64_t)row * p.ldd;
+#pragma unroll
+          for (int j = 0; j < T::FN; ++j) {
+            const int col = n0 + wn * T::TN + j * 16 + fr;
+            if (col < p.n) drow[col] = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
+          }
+        }
     }
+  }
 }
 
-template <int BM, int BN>
-hipError_t launch_tile(int layout, const GemmParams& p, hipStream_t stream) {
-  const int groups = layout == kDense ? 1 : (layout == kMasked ? p.num_groups : 1);
-  const dim3 grid((p.n + BN - 1) / BN, (p.m + BM - 1) / BM, groups);
-  const dim3 block(kThreads);
-  switch (layout) {
-    case kDense:
-      hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, kDense>), grid, block, 0, stream, p);
-      break;
-    case kContiguous:
-      hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, kContiguous>), grid, block, 0, stream, p);
-      break;
-    default:
-      hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, kMasked>), grid, block, 0, stream, p);
-      break;
-  }
+// ------------------------------------------------------------------ host side
+
+// Kernel instances (tile shape, wave grid, pipeline depth).
+using TileP256 = Tile<256, 256, 2, 4, 2>;  // prefill: 8 waves, 128x64 per wave
+using TileP128 = Tile<128, 128, 2, 2, 4>;  // mid-size: 4 waves, 64x64 per wave
+using TileD128 = Tile<128, 64, 2, 2, 4>;   // decode, M <= 128: 64x32 per wave
+using TileD64 = Tile<64, 128, 1, 4, 4>;    // decode, M <= 64: 64x32 per wave
+
+struct Variant {
+  int bm, bn, threads;
+};
+constexpr Variant kVariants[] = {
+    {TileP256::BM, TileP256::BN, TileP256::kThreads},
+    {TileP128::BM, TileP128::BN, TileP128::kThreads},
+    {TileD128::BM, TileD128::BN, TileD128::kThreads},
+    {TileD64::BM, TileD64::BN, TileD64::kThreads},
+};
+constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+
+template <class T, int LAYOUT>
+hipError_t launch_one(const GemmParams& p, const Schedule& s, int grid, hipStream_t stream) {
+  if (s.split_k > 1)
+    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
+  else
+    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, false>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
   return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_layout(int layout, const GemmParams& p, const Schedule& s, int grid, hipStream_t stream) {
+  switch (layout) {
+    case kDense: return launch_one<T, kDense>(p, s, grid, stream);
+    case kContiguous: return launch_one<T, kContiguous>(p, s, grid, stream);
+    default: return launch_one<T, kMasked>(p, s, grid, stream);
+  }
+}
+
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+int forced_variant() {
+  const char* e = getenv("DG_FORCE_CONFIG");  // "variant:split_k", for sweeps
+  if (!e || !*e) return -1;
+  return atoi(e);
+}
+
+int forced_split() {
+  const char* e = getenv("DG_FORCE_CONFIG");
+  if (!e || !*e) return 0;
+  const char* c = strchr(e, ':');
+  return c ? atoi(c + 1) : 0;
 }
 
 }  // namespace
 
 GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cus) {
-  (void)k;
+  // m: dense M, contiguous M_total, masked M_max (expected rows are folded in
+  // by the caller through `groups` tiles; see below).
+  const int nkb = k / kBlockK;
+  // Rows per group that the kernel will actually see.
+  const int rows = m;
+  int v;
+  if (rows <= 64) v = 3;
+  else if (rows <= 128) v = 2;
+  else {
+    const int t256 = cdiv(rows, 256) * cdiv(n, 256) * (layout == kMasked ? groups : 1);
+    v = t256 >= num_cus / 2 ? 0 : 1;
+  }
+  const int fv = forced_variant();
+  if (fv >= 0 && fv < kNumVariants) v = fv;
   GemmConfig c{};
-  c.bm = 128;
-  c.bn = 128;
-  c.split_k = 1;
-  c.variant = 0;
-  const int mt = (m + c.bm - 1) / c.bm;
-  const int nt = (n + c.bn - 1) / c.bn;
-  c.tiles = mt * nt * (layout == kMasked ? groups : 1);
-  c.grid = c.tiles;
-  (void)num_cus;
+  c.variant = v;
+  c.bm = kVariants[v].bm;
+  c.bn = kVariants[v].bn;
+  const int m_tiles = cdiv(rows, c.bm) * (layout == kMasked ? groups : 1);
+  const int n_tiles = cdiv(n, c.bn);
+  c.tiles = m_tiles * n_tiles;
+  // Split K when the tiles alone cannot fill the CUs, keeping >= 4 slices per
+  // split so the pipeline has something to overlap.
+  int split = 1;
+  if (c.tiles < num_cus && nkb >= 8) {
+    split = num_cus / c.tiles;
+    split = split < 1 ? 1 : split;
+    const int max_split = nkb / 4;
+    if (split > max_split) split = max_split;
+    if (split < 1) split = 1;
+  }
+  const int fs = forced_split();
+  if (fs > 0) split = fs < nkb ? fs : (nkb > 0 ? nkb : 1);
+  // A contiguous tile that straddles two experts runs two passes; split-K
+  // bookkeeping assumes one pass per unit, so the contiguous layout never
+  // splits (its M is large anyway).
+  if (nkb == 0 || layout == kContiguous) split = 1;
+  c.split_k = split;
+  // Split-K: launch every unit (tiles * split <= CUs, so all valid units are
+  // resident together; units past the last tile exit at once).  Otherwise a
+  // persistent grid of at most one workgroup per CU.
+  const int units = split > 1 ? cdiv(c.tiles, 8) * 8 * split : c.tiles;
+  c.grid = split > 1 ? units : (units < num_cus ? units : num_cus);
+  if (c.grid < 1) c.grid = 1;
+  c.group_m = 8;
   return c;
 }
 
 size_t workspace_bytes_for(const GemmConfig& cfg, int layout, int m, int n, int groups) {
-  (void)cfg; (void)layout; (void)m; (void)n; (void)groups;
-  return 0;
+  (void)layout; (void)m; (void)n; (void)groups;
+  if (cfg.split_k <= 1) return 0;
+  const size_t tiles = (size_t)cfg.tiles;
+  const size_t partial = tiles * cfg.split_k * (size_t)cfg.bm * cfg.bn * sizeof(float);
+  return partial + tiles * sizeof(int);
 }
 
-hipError_t launch_gemm(int layout, const GemmParams& p, const GemmConfig& cfg,
+hipError_t launch_gemm(int layout, const GemmParams& p0, const GemmConfig& cfg,
                        hipStream_t stream) {
-  (void)cfg;
-  return launch_tile<128, 128>(layout, p, stream);
+  GemmParams p = p0;
+  const int nkb = p.k / kBlockK;
+  Schedule s{};
+  s.split_k = cfg.split_k;
+  s.kb_per_split = cfg.split_k > 1 ? cdiv(nkb, cfg.split_k) : nkb;
+  s.n_tiles = cdiv(p.n, cfg.bn);
+  s.m_tiles = cfg.tiles / s.n_tiles;
+  s.tiles = cfg.tiles;
+  s.units = cfg.split_k > 1 ? cdiv(cfg.tiles, 8) * 8 * cfg.split_k : cfg.tiles;
+  s.group_m = cfg.group_m;
+  if (cfg.split_k > 1) {
+    const size_t partial = (size_t)cfg.tiles * cfg.split_k * (size_t)cfg.bm * cfg.bn * sizeof(float);
+    p.counters = reinterpret_cast<int*>(reinterpret_cast<char*>(p.workspace) + partial);
+  }
+  switch (cfg.variant) {
+    case 0: return launch_layout<TileP256>(layout, p, s, cfg.grid, stream);
+    case 1: return launch_layout<TileP128>(layout, p, s, cfg.grid, stream);
+    case 2: return launch_layout<TileD128>(layout, p, s, cfg.grid, stream);
+    default: return launch_layout<TileD64>(layout, p, s, cfg.grid, stream);
+  }
 }
 
 }  // namespace dg

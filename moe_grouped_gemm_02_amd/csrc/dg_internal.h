@@ -29,12 +29,24 @@ struct GemmParams {
 
 // Tile configuration chosen on the host (deterministically, from the shape).
 struct GemmConfig {
+  int variant;   // kernel instance (tile shape), index into the kernel table
   int bm;
   int bn;
   int split_k;   // number of K ranges per output tile (1 = none)
-  int grid;      // workgroups launched
-  int tiles;     // output tiles (per split) over all groups
-  int variant;   // kernel family index
+  int grid;      // workgroups launched (persistent)
+  int tiles;     // output tiles over all groups (masked: worst case)
+  int group_m;   // raster group height in M tiles
+};
+
+// What the device needs to walk the work units of one launch.
+struct Schedule {
+  int units;         // tiles * split_k
+  int tiles;
+  int m_tiles;       // M tiles (masked: worst-case total over groups)
+  int n_tiles;
+  int split_k;
+  int kb_per_split;  // K slices per split
+  int group_m;
 };
 
 GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cus);

@@ -25,7 +25,7 @@ def _operands(m, n, k, seed, groups=None, a_shape=None):
 
 def _workspace(dg, m, n, k, groups=1):
     size = dg.dg_get_workspace_size(m, n, k, groups)
-    return torch.empty(max(size, 16), dtype=torch.uint8, device="cuda") if size else None
+    return torch.zeros(max(size, 16), dtype=torch.uint8, device="cuda") if size else None
 
 
 def run_dense(dg, a, sfa, b, sfb, ldd=None):

@@ -73,7 +73,7 @@ def test_dense_workload_sampled(wl):
     qb, sfb = _quant_b(dg, xb, 1)
     ws = dg.dg_get_workspace_size(m, n, k, 1)
     d = torch.full((m, n), SENTINEL, dtype=torch.int16, device="cuda")
-    dg.dg_fp8_gemm_nt(a, sfa, qb, sfb, d, workspace=torch.empty(ws, dtype=torch.uint8, device="cuda") if ws else None)
+    dg.dg_fp8_gemm_nt(a, sfa, qb, sfb, d, workspace=torch.zeros(ws, dtype=torch.uint8, device="cuda") if ws else None)
     torch.cuda.synchronize()
 
     rows = _sample_rows(m, 12, rng)
@@ -104,7 +104,7 @@ def test_contiguous_workload_sampled():
     qb, sfb = _quant_b(dg, xb, g)
     ws = dg.dg_get_workspace_size(m_total, n, k, g)
     d = torch.full((m_total, n), SENTINEL, dtype=torch.int16, device="cuda")
-    dg.dg_grouped_contiguous(a, sfa, qb, sfb, d, dev(mi), workspace=torch.empty(ws, dtype=torch.uint8, device="cuda") if ws else None)
+    dg.dg_grouped_contiguous(a, sfa, qb, sfb, d, dev(mi), workspace=torch.zeros(ws, dtype=torch.uint8, device="cuda") if ws else None)
     torch.cuda.synchronize()
     assert not bool((d == SENTINEL).any())
 
@@ -143,7 +143,7 @@ def test_masked_workload_sampled():
     ws = dg.dg_get_workspace_size(m_max, n, k, g)
     d = torch.full((g, m_max, n), SENTINEL, dtype=torch.int16, device="cuda")
     dg.dg_grouped_masked(a, sfa, qb, sfb, d, dev(mm), expected_m=int(mm.mean()),
-                         workspace=torch.empty(ws, dtype=torch.uint8, device="cuda") if ws else None)
+                         workspace=torch.zeros(ws, dtype=torch.uint8, device="cuda") if ws else None)
     torch.cuda.synchronize()
 
     d_h = host(d)
