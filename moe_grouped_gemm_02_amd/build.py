@@ -30,6 +30,8 @@ FLAGS = [
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs, where the promotion FMAs read them (no AGPR copies)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -65,9 +65,11 @@ __device__ __forceinline__ void dma16(uint32_t lds, const void* base, uint32_t o
 // then barrier.  The "memory" clobber keeps the compiler from moving LDS or
 // global accesses across it.
 template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" : : "n"(N) : "memory");
 }
+
+__device__ __forceinline__ void barrier_all() { asm volatile("s_barrier" : : : "memory"); }
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
@@ -104,18 +106,31 @@ struct Tile {
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
   static constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 fragments per wave
+  // DMA instruction i of a stage fills LDS bytes [1024 i, 1024 i + 1024).
+  // Instruction i = j * kWaves + wave, so every wave's j-th instruction falls
+  // in the same region (A rows, B rows, scales) - a compile-time choice.
   static constexpr int kAInstr = BM / 8;            // 1 KB DMA instructions per slice
   static constexpr int kBInstr = BN / 8;
-  static constexpr int kSInstr = (BM / 4 + 63) / 64; // fp32 activation scales
-  static constexpr int kInstr = kAInstr + kBInstr + kSInstr;
-  static constexpr int kLPW = (kInstr + kWaves - 1) / kWaves;  // DMA per wave per stage
-  static constexpr int kStageBytes = kLPW * kWaves * 1024;
+  static constexpr int kAJ = kAInstr / kWaves;      // per-wave instruction counts
+  static constexpr int kBJ = kBInstr / kWaves;
+  static constexpr int kLPW = kAJ + kBJ;            // A/B DMAs per wave per stage; wave 0
+                                                    // issues one more, for the scales
+  static constexpr int kSOffInstr = kAInstr + kBInstr;
+  static constexpr int kStageBytes = (kAInstr + kBInstr + 1) * 1024;
+  static constexpr int kSBCap = 3072;               // weight scales staged per unit (floats):
+                                                    // 3 column blocks x 1024 slices (K <= 131072)
   static constexpr int kBOff = BM * 128;
   static constexpr int kSOff = (BM + BN) * 128;
   static constexpr bool kOneSB = (128 % TN) == 0;   // wave columns inside one 128-block
-  static_assert(TM % 16 == 0 && TN % 16 == 0 && BM % 8 == 0 && BN % 8 == 0, "bad tile");
+  // Overlap the MFMAs of fragment row i+1 with the FMAs of row i (needs a
+  // second set of result registers; with two waves per SIMD the other wave
+  // provides the overlap instead).
+  static constexpr bool kPipe = kWaves <= 4;
+  static_assert(TM % 16 == 0 && TN % 16 == 0, "bad tile");
+  static_assert(kAInstr % kWaves == 0 && kBInstr % kWaves == 0, "tile rows must split evenly over waves");
+  static_assert(BM <= 256, "one scale instruction covers 256 rows");
   static_assert(STAGES >= 2, "need two stages");
-  static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS overflow");
+  static_assert(STAGES * kStageBytes + kSBCap * 4 <= 160 * 1024, "LDS overflow");
 };
 
 // Decode a linear work-unit index into a tile.  XCD-aware: workgroup w runs on
@@ -145,6 +160,7 @@ __device__ __forceinline__ int clamp_rows(int v, int hi) { return v < 0 ? 0 : (v
 template <class T, int LAYOUT, bool SPLIT>
 __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedule s) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::STAGES * T::kStageBytes];
+  __shared__ float sb_lds[T::kSBCap];  // weight scales of the unit: [column block][slice]
   __shared__ int last_flag;
 
   const int tid = threadIdx.x;
@@ -250,27 +266,38 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
       auto issue_stage = [&](int kb, int buf) {
         const uint32_t stage_lds = smem_base + buf * T::kStageBytes;
 #pragma unroll
-        for (int j = 0; j < T::kLPW; ++j) {
-          const int instr = j * T::kWaves + wave;  // wave-uniform
-          if (instr < T::kAInstr) {
-            const int q = instr * 64 + lane;
-            const int r = q >> 3, c = (q & 7) ^ (r & 7);
-            const int gr = min(m0 + r, rows_valid - 1);
-            dma16(stage_lds + instr * 1024, A, (uint32_t)gr * (uint32_t)p.lda + kb * 128 + c * 16);
-          } else if (instr < T::kAInstr + T::kBInstr) {
-            const int q = (instr - T::kAInstr) * 64 + lane;
-            const int r = q >> 3, c = (q & 7) ^ (r & 7);
-            const int gn = min(n0 + r, p.n - 1);
-            dma16(stage_lds + instr * 1024, B, (uint32_t)gn * (uint32_t)p.ldb + kb * 128 + c * 16);
-          } else if (instr < T::kAInstr + T::kBInstr + T::kSInstr) {
-            const int q = (instr - T::kAInstr - T::kBInstr) * 64 + lane;
-            const int r4 = min(m0 + 4 * q, (int)p.ld_sfa - 4);
-            dma16(stage_lds + instr * 1024, SA, (uint32_t)(kb * p.ld_sfa + r4) * 4u);
-          } else {
-            dma16(stage_lds + instr * 1024, A, 0u);  // padding
-          }
+        for (int j = 0; j < T::kAJ; ++j) {
+          const int instr = j * T::kWaves + wave;
+          const int q = instr * 64 + lane;
+          const int r = q >> 3, c = (q & 7) ^ (r & 7);
+          const int gr = min(m0 + r, rows_valid - 1);
+          dma16(stage_lds + instr * 1024, A, (uint32_t)gr * (uint32_t)p.lda + kb * 128 + c * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < T::kBJ; ++j) {
+          const int instr = (T::kAJ + j) * T::kWaves + wave;
+          const int q = (j * T::kWaves + wave) * 64 + lane;
+          const int r = q >> 3, c = (q & 7) ^ (r & 7);
+          const int gn = min(n0 + r, p.n - 1);
+          dma16(stage_lds + instr * 1024, B, (uint32_t)gn * (uint32_t)p.ldb + kb * 128 + c * 16);
+        }
+        if (wave == 0) {
+          // Activation scales of the slice: rows m0 .. m0 + 4*63 + 3.
+          const int r4 = min(m0 + 4 * lane, (int)p.ld_sfa - 4);
+          dma16(stage_lds + T::kSOffInstr * 1024, SA, (uint32_t)(kb * p.ld_sfa + r4) * 4u);
         }
       };
+
+      // Weight scales of this unit into LDS: column blocks cb_first .. cb_last
+      // of the tile, slices kb0 .. kb1 (the loop then reads them from LDS and
+      // issues no vector memory operation besides the stage DMAs).
+      const int cb_first = n0 >> 7;
+      const int cb_count = min((n0 + T::BN - 1) >> 7, n_blocks - 1) - cb_first + 1;
+      lds_barrier();  // previous unit's readers are done with every LDS buffer
+      for (int idx = tid; idx < min(cb_count * nkb, T::kSBCap); idx += T::kThreads) {
+        const int cbi = idx / nkb, kk = idx - cbi * nkb;
+        sb_lds[idx] = SB[(cb_first + cbi) * nkb_total + kb0 + kk];
+      }
 
       v4f acc[T::FM][T::FN];
 #pragma unroll
@@ -278,28 +305,33 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
 #pragma unroll
         for (int j = 0; j < T::FN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-      lds_barrier();  // previous unit's readers are done with every buffer
 #pragma unroll
       for (int st = 0; st < T::STAGES - 1; ++st)
         if (st < nkb) issue_stage(kb0 + st, st);
 
       for (int it = 0; it < nkb; ++it) {
-        if (it + T::STAGES - 2 < nkb) wait_vm_barrier<(T::STAGES - 2) * T::kLPW>();
-        else wait_vm_barrier<0>();
+        // Wait for this wave's DMAs of stage `it` (newer stages may stay in
+        // flight), then barrier so every wave's part of the stage has landed.
+        if (it + T::STAGES - 2 < nkb) {
+          if (wave == 0) wait_vm<(T::STAGES - 2) * (T::kLPW + 1)>();
+          else wait_vm<(T::STAGES - 2) * T::kLPW>();
+        } else {
+          wait_vm<0>();
+        }
+        barrier_all();
         if (it + T::STAGES - 1 < nkb) issue_stage(kb0 + it + T::STAGES - 1, (it + T::STAGES - 1) % T::STAGES);
 
-        const int kb = kb0 + it;
         const uint8_t* st = smem + (it % T::STAGES) * T::kStageBytes;
         float sbw = 0.0f;
         float sbv[T::FN];
         if (T::kOneSB) {
           const int cb = min((n0 + wn * T::TN) >> 7, n_blocks - 1);
-          sbw = SB[cb * nkb_total + kb];
+          sbw = sb_lds[(cb - cb_first) * nkb + it];
         } else {
 #pragma unroll
           for (int j = 0; j < T::FN; ++j) {
             const int cb = min((n0 + wn * T::TN + j * 16) >> 7, n_blocks - 1);
-            sbv[j] = SB[cb * nkb_total + kb];
+            sbv[j] = sb_lds[(cb - cb_first) * nkb + it];
           }
         }
         v8i bfrag[T::FN];
@@ -309,76 +341,172 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
           bfrag[j] = make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
                               *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
         }
+        // Software pipeline over the fragment rows: the MFMAs of row i+1 are
+        // issued into a second set of result registers before the promotion
+        // FMAs of row i, so the matrix core and the VALU overlap instead of
+        // each FMA waiting on the MFMA just issued.
+        auto load_a = [&](int i) {
+          const uint8_t* rowp = st + (wm * T::TM + i * 16 + fr) * 128;
+          return make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
+                          *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
+        };
+        auto load_s = [&](int i) {
+          return *reinterpret_cast<const float4*>(st + T::kSOff + (wm * T::TM + i * 16 + 4 * kg) * 4);
+        };
+        v4f part[T::kPipe ? 2 : 1][T::FN];
+        v8i afrag = load_a(0);
+        if (T::kPipe) {
+#pragma unroll
+          for (int j = 0; j < T::FN; ++j) part[0][j] = mfma_fp8_slice(afrag, bfrag[j]);
+        }
 #pragma unroll
         for (int i = 0; i < T::FM; ++i) {
-          const uint8_t* rowp = st + (wm * T::TM + i * 16 + fr) * 128;
-          const v8i afrag = make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
-                                     *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
-          const float4 s4 = *reinterpret_cast<const float4*>(st + T::kSOff + (wm * T::TM + i * 16 + 4 * kg) * 4);
-          const float sa[4] = {s4.x, s4.y, s4.z, s4.w};
+          const int cur = T::kPipe ? (i & 1) : 0;
+          const float4 s4 = load_s(i);
+          if (T::kPipe) {
+            if (i + 1 < T::FM) {
+              afrag = load_a(i + 1);
 #pragma unroll
-          for (int j = 0; j < T::FN; ++j) {
-            const v4f part = mfma_fp8_slice(afrag, bfrag[j]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float sc = T::kOneSB ? sa[e] * sbw : sa[e] * sbv[j];
-              acc[i][j][e] = fmaf(part[e], sc, acc[i][j][e]);
+              for (int j = 0; j < T::FN; ++j) part[cur ^ 1][j] = mfma_fp8_slice(afrag, bfrag[j]);
             }
+          } else {
+            if (i > 0) afrag = load_a(i);
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j) part[0][j] = mfma_fp8_slice(afrag, bfrag[j]);
           }
+          const float sa[4] = {s4.x, s4.y, s4.z, s4.w};
+          float sc[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[e] = T::kOneSB ? sa[e] * sbw : 0.0f;
+#pragma unroll
+          for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[i][j][e] = fmaf(part[cur][j][e], T::kOneSB ? sc[e] : sa[e] * sbv[j], acc[i][j][e]);
         }
       }
 
       // ------------------------------------------------------- split-K fixup
       if (SPLIT && s.split_k > 1) {
-        float4* ws = reinterpret_cast<float4*>(p.workspace);
+        // Partials go through agent-scope (sc1) stores and loads, which are
+        // coherent across XCDs without a cache-wide write-back.  Each thread
+        // waits for its stores to complete before the barrier; the arrival
+        // counter is bumped after the barrier, so a unit that sees the count
+        // reach split_k - 1 reads complete partials.
+        uint64_t* ws = reinterpret_cast<uint64_t*>(p.workspace);
         const int fr_per = T::FM * T::FN;
-        float4* mine = ws + ((int64_t)(t * s.split_k + split) * fr_per) * T::kThreads;
+        uint64_t* mine = ws + ((int64_t)(t * s.split_k + split) * fr_per) * T::kThreads * 2;
 #pragma unroll
         for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-          for (int j = 0; j < T::FN; ++j)
-            mine[(i * T::FN + j) * T::kThreads + tid] = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-        __threadfence();
+          for (int j = 0; j < T::FN; ++j) {
+            uint64_t* dst = mine + ((i * T::FN + j) * T::kThreads + tid) * 2;
+            const uint64_t lo = ((uint64_t)__float_as_uint(acc[i][j][1]) << 32) | __float_as_uint(acc[i][j][0]);
+            const uint64_t hi = ((uint64_t)__float_as_uint(acc[i][j][3]) << 32) | __float_as_uint(acc[i][j][2]);
+            __hip_atomic_store(dst, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(dst + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
         __syncthreads();
         if (tid == 0) {
-          const int old = atomicAdd(&p.counters[t], 1);
+          const int old = __hip_atomic_fetch_add(&p.counters[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           last_flag = (old == s.split_k - 1);
         }
         __syncthreads();
         if (!last_flag) continue;
-        __threadfence();
         // Sum every split's partial, this unit's own included, in split order.
 #pragma unroll
         for (int i = 0; i < T::FM; ++i)
 #pragma unroll
           for (int j = 0; j < T::FN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        for (int sp = 0; sp < s.split_k; ++sp) {
-          const float4* src = ws + ((int64_t)(t * s.split_k + sp) * fr_per) * T::kThreads;
+        for (int sp = 0; sp < s.split_k; sp += 2) {
+          // Two splits' loads in flight at once; summed in split order.
+          const bool two = sp + 1 < s.split_k;
+          uint64_t* src0 = ws + ((int64_t)(t * s.split_k + sp) * fr_per) * T::kThreads * 2;
+          uint64_t* src1 = two ? src0 + (int64_t)fr_per * T::kThreads * 2 : src0;
+          uint64_t v0[T::FM][T::FN][2], v1[T::FM][T::FN][2];
 #pragma unroll
           for (int i = 0; i < T::FM; ++i)
 #pragma unroll
-            for (int j = 0; j < T::FN; ++j)
-              acc[i][j] += *reinterpret_cast<const v4f*>(src + (i * T::FN + j) * T::kThreads + tid);
+            for (int j = 0; j < T::FN; ++j) {
+              const int64_t e = ((i * T::FN + j) * T::kThreads + tid) * 2;
+              v0[i][j][0] = __hip_atomic_load(src0 + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              v0[i][j][1] = __hip_atomic_load(src0 + e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              v1[i][j][0] = __hip_atomic_load(src1 + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              v1[i][j][1] = __hip_atomic_load(src1 + e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+          for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j) {
+              acc[i][j] += v4f{__uint_as_float((uint32_t)v0[i][j][0]), __uint_as_float((uint32_t)(v0[i][j][0] >> 32)),
+                               __uint_as_float((uint32_t)v0[i][j][1]), __uint_as_float((uint32_t)(v0[i][j][1] >> 32))};
+              if (two)
+                acc[i][j] += v4f{__uint_as_float((uint32_t)v1[i][j][0]), __uint_as_float((uint32_t)(v1[i][j][0] >> 32)),
+                                 __uint_as_float((uint32_t)v1[i][j][1]), __uint_as_float((uint32_t)(v1[i][j][1] >> 32))};
+            }
         }
-        if (tid == 0) p.counters[t] = 0;  // ready for the next call
+        if (tid == 0) __hip_atomic_store(&p.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
 
       // ------------------------------------------------------------ epilogue
+      // bf16 (RNE) tile staged through LDS, then stored as 16-byte row chunks.
+      // A lane holds column fr of rows 4kg..4kg+3 of each fragment; lane pairs
+      // (fr, fr^1) swap halves so each lane writes two rows of two adjacent
+      // columns as 32-bit words.
+      constexpr int kRowBytes = T::BN * 2 + 32;
+      constexpr int kER = (T::BM * kRowBytes <= T::STAGES * T::kStageBytes) ? T::BM : T::TM;
+      static_assert(kER * kRowBytes <= T::STAGES * T::kStageBytes, "epilogue tile does not fit");
+      static_assert(kER == T::BM || kER == T::TM, "epilogue pass must be whole wave rows");
+      const bool odd = fr & 1;
 #pragma unroll
-      for (int i = 0; i < T::FM; ++i)
+      for (int er = 0; er < T::BM / kER; ++er) {
+        lds_barrier();  // LDS free: the K loop (or previous pass) is done reading
+        if (kER == T::BM || wm == er) {
+          const int rbase = (kER == T::BM) ? wm * T::TM : 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = m0 + wm * T::TM + i * 16 + 4 * kg + e;
+          for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j) {
+              const uint32_t b0 = f32_to_bf16_rne(acc[i][j][0]), b1 = f32_to_bf16_rne(acc[i][j][1]);
+              const uint32_t b2 = f32_to_bf16_rne(acc[i][j][2]), b3 = f32_to_bf16_rne(acc[i][j][3]);
+              const uint32_t send = odd ? (b0 | (b1 << 16)) : (b2 | (b3 << 16));
+              const uint32_t recv = (uint32_t)__shfl_xor((int)send, 1, 64);
+              uint32_t w0, w1;
+              if (odd) {  // rows 4kg+2, 4kg+3; columns fr-1, fr
+                w0 = (recv & 0xFFFFu) | (b2 << 16);
+                w1 = (recv >> 16) | (b3 << 16);
+              } else {    // rows 4kg+0, 4kg+1; columns fr, fr+1
+                w0 = b0 | ((recv & 0xFFFFu) << 16);
+                w1 = b1 | ((recv >> 16) << 16);
+              }
+              const int r = rbase + i * 16 + 4 * kg + (odd ? 2 : 0);
+              const int c = wn * T::TN + j * 16 + (fr & ~1);
+              uint8_t* dst = smem + r * kRowBytes + c * 2;
+              *reinterpret_cast<uint32_t*>(dst) = w0;
+              *reinterpret_cast<uint32_t*>(dst + kRowBytes) = w1;
+            }
+        }
+        lds_barrier();
+        constexpr int kChunksPerRow = T::BN / 8;
+        for (int idx = tid; idx < kER * kChunksPerRow; idx += T::kThreads) {
+          const int rl = idx / kChunksPerRow, ch = idx - rl * kChunksPerRow;
+          const int row = m0 + er * kER + rl;
           bool ok = row < rows_valid && row < m0 + T::BM;
           if (LAYOUT == kContiguous && ok) ok = p.m_indices[row] == g;
           if (!ok) continue;
+          const int col = n0 + ch * 8;
+          if (col >= p.n) continue;
+          const uint4 v = *reinterpret_cast<const uint4*>(smem + rl * kRowBytes + ch * 16);
           uint16_t* drow = D + (int64_t)row * p.ldd;
-#pragma unroll
-          for (int j = 0; j < T::FN; ++j) {
-            const int col = n0 + wn * T::TN + j * 16 + fr;
-            if (col < p.n) drow[col] = (uint16_t)f32_to_bf16_rne(acc[i][j][e]);
+          if (col + 8 <= p.n) {
+            *reinterpret_cast<uint4*>(drow + col) = v;
+          } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (int e = 0; e < p.n - col; ++e) drow[col + e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
           }
         }
+      }
     }
   }
 }
@@ -387,9 +515,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
 
 // Kernel instances (tile shape, wave grid, pipeline depth).
 using TileP256 = Tile<256, 256, 2, 4, 2>;  // prefill: 8 waves, 128x64 per wave
-using TileP128 = Tile<128, 128, 2, 2, 4>;  // mid-size: 4 waves, 64x64 per wave
-using TileD128 = Tile<128, 64, 2, 2, 4>;   // decode, M <= 128: 64x32 per wave
-using TileD64 = Tile<64, 128, 1, 4, 4>;    // decode, M <= 64: 64x32 per wave
+using TileP128 = Tile<128, 128, 2, 2, 4>;  // mid-size and decode M <= 128: 64x64 per wave
+using TileD128 = Tile<128, 64, 2, 2, 4>;   // decode, narrow N tiles: 64x32 per wave
+using TileD64 = Tile<64, 256, 1, 4, 3>;    // decode, M <= 64: 64x64 per wave
+using TileS64 = Tile<64, 64, 2, 2, 8>;     // decode, small tiles, deep pipeline: 32x32 per wave
 
 struct Variant {
   int bm, bn, threads;
@@ -399,12 +528,13 @@ constexpr Variant kVariants[] = {
     {TileP128::BM, TileP128::BN, TileP128::kThreads},
     {TileD128::BM, TileD128::BN, TileD128::kThreads},
     {TileD64::BM, TileD64::BN, TileD64::kThreads},
+    {TileS64::BM, TileS64::BN, TileS64::kThreads},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 template <class T, int LAYOUT>
 hipError_t launch_one(const GemmParams& p, const Schedule& s, int grid, hipStream_t stream) {
-  if (s.split_k > 1)
+  if (s.split_k > 1 && T::BM * T::BN < 256 * 256)  // the 256x256 tile never splits
     hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
   else
     hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, false>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
@@ -445,7 +575,7 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
   const int rows = m;
   int v;
   if (rows <= 64) v = 3;
-  else if (rows <= 128) v = 2;
+  else if (rows <= 128) v = 1;
   else {
     const int t256 = cdiv(rows, 256) * cdiv(n, 256) * (layout == kMasked ? groups : 1);
     v = t256 >= num_cus / 2 ? 0 : 1;
@@ -473,8 +603,9 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
   if (fs > 0) split = fs < nkb ? fs : (nkb > 0 ? nkb : 1);
   // A contiguous tile that straddles two experts runs two passes; split-K
   // bookkeeping assumes one pass per unit, so the contiguous layout never
-  // splits (its M is large anyway).
-  if (nkb == 0 || layout == kContiguous) split = 1;
+  // splits (its M is large anyway).  Nor does the 256x256 tile (its
+  // accumulators leave no registers for the reduction).
+  if (nkb == 0 || layout == kContiguous || c.bm * c.bn >= 256 * 256) split = 1;
   c.split_k = split;
   // Split-K: launch every unit (tiles * split <= CUs, so all valid units are
   // resident together; units past the last tile exit at once).  Otherwise a
@@ -514,7 +645,8 @@ hipError_t launch_gemm(int layout, const GemmParams& p0, const GemmConfig& cfg,
     case 0: return launch_layout<TileP256>(layout, p, s, cfg.grid, stream);
     case 1: return launch_layout<TileP128>(layout, p, s, cfg.grid, stream);
     case 2: return launch_layout<TileD128>(layout, p, s, cfg.grid, stream);
-    default: return launch_layout<TileD64>(layout, p, s, cfg.grid, stream);
+    case 3: return launch_layout<TileD64>(layout, p, s, cfg.grid, stream);
+    default: return launch_layout<TileS64>(layout, p, s, cfg.grid, stream);
   }
 }
 
