@@ -31,7 +31,7 @@
  *     empty sum); then a, b, sfa and sfb are not read and may be NULL.
  *
  * Shape and alignment rules (checked; DG_ERR_* on violation)
- *   - k % 128 == 0 and k <= 131072 (DG_ERR_UNSUPPORTED_SHAPE); m, n >= 0.
+ *   - k % 128 == 0 (DG_ERR_UNSUPPORTED_SHAPE); m, n arbitrary >= 0.
  *   - a, b, d, sfa, sfb 16-byte aligned; lda, ldb multiples of 16 (bytes =
  *     elements); ldd a multiple of 8 elements; ld_sfa a multiple of 4 and
  *     >= the rows it covers (DG_ERR_MISALIGNED / DG_ERR_INVALID_VALUE).

@@ -71,7 +71,6 @@ int check_gemm_common(const uint8_t* a, const float* sfa, const uint8_t* b, cons
                       int64_t ldd, int64_t ld_sfa) {
   if (rows < 0 || n < 0 || k < 0) return fail(DG_ERR_INVALID_VALUE, "negative dimension (m=%d n=%d k=%d)", rows, n, k);
   if (k % 128 != 0) return fail(DG_ERR_UNSUPPORTED_SHAPE, "k=%d is not a multiple of 128", k);
-  if (k > 131072) return fail(DG_ERR_UNSUPPORTED_SHAPE, "k=%d exceeds 131072", k);
   // With k == 0 nothing of A, B or the scales is read, so only d must be valid.
   if (!d || (k > 0 && (!a || !sfa || !b || !sfb)))
     return fail(DG_ERR_INVALID_VALUE, "null pointer argument");

@@ -61,6 +61,14 @@ __device__ __forceinline__ void dma16(uint32_t lds, const void* base, uint32_t o
                : "memory", "m0");
 }
 
+// 4-byte variant: lane l's dword lands at m0 + 4 * l (256 bytes per instruction).
+__device__ __forceinline__ void dma4(uint32_t lds, const void* base, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(lds), "v"(off), "s"(base)
+               : "memory", "m0");
+}
+
 // Wait until at most N of this wave's vector memory operations are in flight,
 // then barrier.  The "memory" clobber keeps the compiler from moving LDS or
 // global accesses across it.
@@ -113,12 +121,12 @@ struct Tile {
   static constexpr int kBInstr = BN / 8;
   static constexpr int kAJ = kAInstr / kWaves;      // per-wave instruction counts
   static constexpr int kBJ = kBInstr / kWaves;
-  static constexpr int kLPW = kAJ + kBJ;            // A/B DMAs per wave per stage; wave 0
-                                                    // issues one more, for the scales
+  static constexpr int kLPW = kAJ + kBJ;            // A/B DMAs per wave per stage; waves 0
+                                                    // and 1 issue one more each, for the
+                                                    // activation and the weight scales
   static constexpr int kSOffInstr = kAInstr + kBInstr;
-  static constexpr int kStageBytes = (kAInstr + kBInstr + 1) * 1024;
-  static constexpr int kSBCap = 3072;               // weight scales staged per unit (floats):
-                                                    // 3 column blocks x 1024 slices (K <= 131072)
+  static constexpr int kSBOff = (kAInstr + kBInstr + 1) * 1024;  // weight scales of the slice
+  static constexpr int kStageBytes = (kAInstr + kBInstr + 2) * 1024;
   static constexpr int kBOff = BM * 128;
   static constexpr int kSOff = (BM + BN) * 128;
   static constexpr bool kOneSB = (128 % TN) == 0;   // wave columns inside one 128-block
@@ -130,7 +138,8 @@ struct Tile {
   static_assert(kAInstr % kWaves == 0 && kBInstr % kWaves == 0, "tile rows must split evenly over waves");
   static_assert(BM <= 256, "one scale instruction covers 256 rows");
   static_assert(STAGES >= 2, "need two stages");
-  static_assert(STAGES * kStageBytes + kSBCap * 4 <= 160 * 1024, "LDS overflow");
+  static_assert(kWaves >= 2, "waves 0 and 1 load the scales");
+  static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS overflow");
 };
 
 // Decode a linear work-unit index into a tile.  XCD-aware: workgroup w runs on
@@ -160,7 +169,6 @@ __device__ __forceinline__ int clamp_rows(int v, int hi) { return v < 0 ? 0 : (v
 template <class T, int LAYOUT, bool SPLIT>
 __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedule s) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::STAGES * T::kStageBytes];
-  __shared__ float sb_lds[T::kSBCap];  // weight scales of the unit: [column block][slice]
   __shared__ int last_flag;
 
   const int tid = threadIdx.x;
@@ -259,6 +267,9 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
       const float* SB = uniform_ptr(p.sfb + (int64_t)g * p.sfb_gstride);
       const int nkb = kb1 - kb0;
 
+      const int cb_first = n0 >> 7;  // the tile's 128-column weight-scale blocks
+      const int cb_count = min((n0 + T::BN - 1) >> 7, n_blocks - 1) - cb_first + 1;
+
       // Stage loader.  DMA instruction i of a stage fills LDS bytes
       // [1024 i, 1024 i + 1024): instructions [0, BM/8) carry A rows,
       // [BM/8, (BM+BN)/8) B rows, then the BM activation scales, then padding
@@ -285,19 +296,15 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
           // Activation scales of the slice: rows m0 .. m0 + 4*63 + 3.
           const int r4 = min(m0 + 4 * lane, (int)p.ld_sfa - 4);
           dma16(stage_lds + T::kSOffInstr * 1024, SA, (uint32_t)(kb * p.ld_sfa + r4) * 4u);
+        } else if (wave == 1) {
+          // Weight scales of the slice for the tile's column blocks (lane l:
+          // block cb_first + l; lanes past the last block repeat it).
+          const int cb = cb_first + min(lane, cb_count - 1);
+          dma4(stage_lds + T::kSBOff, SB, (uint32_t)(cb * nkb_total + kb) * 4u);
         }
       };
 
-      // Weight scales of this unit into LDS: column blocks cb_first .. cb_last
-      // of the tile, slices kb0 .. kb1 (the loop then reads them from LDS and
-      // issues no vector memory operation besides the stage DMAs).
-      const int cb_first = n0 >> 7;
-      const int cb_count = min((n0 + T::BN - 1) >> 7, n_blocks - 1) - cb_first + 1;
       lds_barrier();  // previous unit's readers are done with every LDS buffer
-      for (int idx = tid; idx < min(cb_count * nkb, T::kSBCap); idx += T::kThreads) {
-        const int cbi = idx / nkb, kk = idx - cbi * nkb;
-        sb_lds[idx] = SB[(cb_first + cbi) * nkb_total + kb0 + kk];
-      }
 
       v4f acc[T::FM][T::FN];
 #pragma unroll
@@ -313,7 +320,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
         // Wait for this wave's DMAs of stage `it` (newer stages may stay in
         // flight), then barrier so every wave's part of the stage has landed.
         if (it + T::STAGES - 2 < nkb) {
-          if (wave == 0) wait_vm<(T::STAGES - 2) * (T::kLPW + 1)>();
+          if (wave < 2) wait_vm<(T::STAGES - 2) * (T::kLPW + 1)>();
           else wait_vm<(T::STAGES - 2) * T::kLPW>();
         } else {
           wait_vm<0>();
@@ -324,14 +331,15 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
         const uint8_t* st = smem + (it % T::STAGES) * T::kStageBytes;
         float sbw = 0.0f;
         float sbv[T::FN];
+        const float* sbs = reinterpret_cast<const float*>(st + T::kSBOff);
         if (T::kOneSB) {
           const int cb = min((n0 + wn * T::TN) >> 7, n_blocks - 1);
-          sbw = sb_lds[(cb - cb_first) * nkb + it];
+          sbw = sbs[cb - cb_first];
         } else {
 #pragma unroll
           for (int j = 0; j < T::FN; ++j) {
             const int cb = min((n0 + wn * T::TN + j * 16) >> 7, n_blocks - 1);
-            sbv[j] = sb_lds[(cb - cb_first) * nkb + it];
+            sbv[j] = sbs[cb - cb_first];
           }
         }
         v8i bfrag[T::FN];
@@ -519,6 +527,7 @@ using TileP128 = Tile<128, 128, 2, 2, 4>;  // mid-size and decode M <= 128: 64x6
 using TileD128 = Tile<128, 64, 2, 2, 4>;   // decode, narrow N tiles: 64x32 per wave
 using TileD64 = Tile<64, 256, 1, 4, 3>;    // decode, M <= 64: 64x64 per wave
 using TileS64 = Tile<64, 64, 2, 2, 8>;     // decode, small tiles, deep pipeline: 32x32 per wave
+using TileW128 = Tile<128, 256, 2, 4, 3>;  // decode, M <= 128, wide N: 8 waves, 64x64 per wave
 
 struct Variant {
   int bm, bn, threads;
@@ -529,15 +538,19 @@ constexpr Variant kVariants[] = {
     {TileD128::BM, TileD128::BN, TileD128::kThreads},
     {TileD64::BM, TileD64::BN, TileD64::kThreads},
     {TileS64::BM, TileS64::BN, TileS64::kThreads},
+    {TileW128::BM, TileW128::BN, TileW128::kThreads},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 template <class T, int LAYOUT>
 hipError_t launch_one(const GemmParams& p, const Schedule& s, int grid, hipStream_t stream) {
-  if (s.split_k > 1 && T::BM * T::BN < 256 * 256)  // the 256x256 tile never splits
-    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
-  else
-    hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, false>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
+  if constexpr (T::BM * T::BN < 256 * 256) {  // the 256x256 tile never splits
+    if (s.split_k > 1) {
+      hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, false>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
   return hipGetLastError();
 }
 
@@ -646,7 +659,8 @@ hipError_t launch_gemm(int layout, const GemmParams& p0, const GemmConfig& cfg,
     case 1: return launch_layout<TileP128>(layout, p, s, cfg.grid, stream);
     case 2: return launch_layout<TileD128>(layout, p, s, cfg.grid, stream);
     case 3: return launch_layout<TileD64>(layout, p, s, cfg.grid, stream);
-    default: return launch_layout<TileS64>(layout, p, s, cfg.grid, stream);
+    case 4: return launch_layout<TileS64>(layout, p, s, cfg.grid, stream);
+    default: return launch_layout<TileW128>(layout, p, s, cfg.grid, stream);
   }
 }
 
