@@ -138,7 +138,11 @@ class Prepared:
         self.sf_bytes = scale_bytes(self.m_valid, n, k, g)
         layout_id = {"dense": 0, "contiguous": 1, "masked": 2}[wl.layout]
         self.config = dg.dg_describe_config(layout_id, self.m_rows, n, k, g, dg.dg_get_num_cus())
-        self.kernel_key = self.config.split(" workspace=")[0]
+        # One kernel instance per (tile variant, layout, split or not): the
+        # unit rocprofv3 reports durations for.
+        fields = dict(kv.split("=") for kv in self.config.split())
+        self.kernel_key = (f"gemm_kernel variant={fields['variant']} bm={fields['bm']} bn={fields['bn']} "
+                           f"layout={wl.layout} split={'yes' if int(fields['split_k']) > 1 else 'no'}")
 
     def quant(self, dg):
         dg.dg_quant_1x128(self.x, self.a, self.sfa)
@@ -155,6 +159,51 @@ class Prepared:
 
 
 # ------------------------------------------------------------------ timing --
+
+class HipEvents:
+    """HIP events created with hipEventDisableSystemFence, through the HIP
+    runtime already loaded in this process (torch's).  Default events add a
+    system-scope fence to every record (a few us per launch on this GPU);
+    these timestamp kernels without it."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("HIP runtime not loaded")
+        self.ct = ctypes
+        self.lib = ctypes.CDLL(path)
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        if self.lib.hipEventCreateWithFlags(self.ct.byref(ev), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        return ev
+
+    def record(self, ev, stream_handle):
+        if self.lib.hipEventRecord(ev, self.ct.c_void_p(stream_handle)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        if self.lib.hipEventElapsedTime(self.ct.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ev)
+
 
 def _enqueue_ahead(torch, enqueue_fn):
     """Run enqueue_fn while the GPU is held by a sleep kernel.
@@ -177,15 +226,23 @@ def _enqueue_ahead(torch, enqueue_fn):
     return host_s, sleep_s > host_s
 
 
-def time_steps(dg, torch, preps, steps, warmup):
-    """Time `steps` whole steps; GEMM launches are bracketed by events too."""
+def time_steps(dg, torch, preps, steps, warmup, hip=None):
+    """Time `steps` whole steps, every GEMM launch bracketed by events.
+
+    Returns (total ms for the steps, per-launch GEMM ms [steps][shapes]).  The
+    step is timed with torch events; the GEMM launches with fence-free HIP
+    events (HipEvents) on the same stream, recorded right before and after
+    each launch.
+    """
+    hip = hip or HipEvents()
     stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
     for w in range(warmup):
         for p in preps:
             p.quant(dg)
             p.gemm(dg, w)
     torch.cuda.synchronize()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in preps] for _ in range(steps)]
+    ev = [[(hip.create(), hip.create()) for _ in preps] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def enqueue():
@@ -193,9 +250,9 @@ def time_steps(dg, torch, preps, steps, warmup):
         for s in range(steps):
             for i, p in enumerate(preps):
                 p.quant(dg)
-                ev[s][i][0].record(stream)
+                hip.record(ev[s][i][0], sh)
                 p.gemm(dg, warmup + s)
-                ev[s][i][1].record(stream)
+                hip.record(ev[s][i][1], sh)
         end.record(stream)
 
     host_s, ahead = _enqueue_ahead(torch, enqueue)
@@ -203,7 +260,11 @@ def time_steps(dg, torch, preps, steps, warmup):
         print(f"warning: host enqueue ({host_s * 1e3:.1f} ms) outlasted the GPU sleep; timings include host gaps",
               file=sys.stderr)
     total_ms = start.elapsed_time(end)
-    gemm_ms = np.array([[a.elapsed_time(b) for (a, b) in row] for row in ev])  # [steps][shapes]
+    gemm_ms = np.array([[hip.elapsed_ms(a, b) for (a, b) in row] for row in ev])  # [steps][shapes]
+    for row in ev:
+        for a, b in row:
+            hip.destroy(a)
+            hip.destroy(b)
     return total_ms, gemm_ms
 
 

@@ -528,6 +528,9 @@ using TileD128 = Tile<128, 64, 2, 2, 4>;   // decode, narrow N tiles: 64x32 per 
 using TileD64 = Tile<64, 256, 1, 4, 3>;    // decode, M <= 64: 64x64 per wave
 using TileS64 = Tile<64, 64, 2, 2, 8>;     // decode, small tiles, deep pipeline: 32x32 per wave
 using TileW128 = Tile<128, 256, 2, 4, 3>;  // decode, M <= 128, wide N: 8 waves, 64x64 per wave
+using TileP128w8 = Tile<128, 128, 2, 4, 4>;  // decode: 8 waves (2 per SIMD), 64x32 per wave
+using TileS64w8 = Tile<64, 64, 2, 4, 8>;     // decode small tiles: 8 waves, 32x16 per wave
+using TileW128w16 = Tile<128, 256, 4, 4, 3>; // decode wide N: 16 waves, 32x64 per wave
 
 struct Variant {
   int bm, bn, threads;
@@ -539,6 +542,9 @@ constexpr Variant kVariants[] = {
     {TileD64::BM, TileD64::BN, TileD64::kThreads},
     {TileS64::BM, TileS64::BN, TileS64::kThreads},
     {TileW128::BM, TileW128::BN, TileW128::kThreads},
+    {TileP128w8::BM, TileP128w8::BN, TileP128w8::kThreads},
+    {TileS64w8::BM, TileS64w8::BN, TileS64w8::kThreads},
+    {TileW128w16::BM, TileW128w16::BN, TileW128w16::kThreads},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -660,7 +666,10 @@ hipError_t launch_gemm(int layout, const GemmParams& p0, const GemmConfig& cfg,
     case 2: return launch_layout<TileD128>(layout, p, s, cfg.grid, stream);
     case 3: return launch_layout<TileD64>(layout, p, s, cfg.grid, stream);
     case 4: return launch_layout<TileS64>(layout, p, s, cfg.grid, stream);
-    default: return launch_layout<TileW128>(layout, p, s, cfg.grid, stream);
+    case 5: return launch_layout<TileW128>(layout, p, s, cfg.grid, stream);
+    case 6: return launch_layout<TileP128w8>(layout, p, s, cfg.grid, stream);
+    case 7: return launch_layout<TileS64w8>(layout, p, s, cfg.grid, stream);
+    default: return launch_layout<TileW128w16>(layout, p, s, cfg.grid, stream);
   }
 }
 
