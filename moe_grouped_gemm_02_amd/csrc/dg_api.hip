@@ -247,8 +247,8 @@ int dg_describe_config(int layout, int m, int n, int k, int num_groups, int num_
       num_groups < 1 || num_cus < 1 || !buf || len == 0)
     return fail(DG_ERR_INVALID_VALUE, "bad arguments to dg_describe_config");
   const dg::GemmConfig c = dg::choose_config(layout, m, n, k, num_groups, num_cus);
-  snprintf(buf, len, "layout=%s bm=%d bn=%d split_k=%d grid=%d tiles=%d variant=%d workspace=%zu",
-           layout_name(layout), c.bm, c.bn, c.split_k, c.grid, c.tiles, c.variant,
+  snprintf(buf, len, "layout=%s bm=%d bn=%d split_k=%d grid=%d tiles=%d variant=%d k_rotate=%d workspace=%zu",
+           layout_name(layout), c.bm, c.bn, c.split_k, c.grid, c.tiles, c.variant, c.k_rotate,
            dg::workspace_bytes_for(c, layout, m, n, num_groups));
   return ok();
 }

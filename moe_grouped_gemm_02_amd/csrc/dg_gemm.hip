@@ -39,6 +39,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+#include <type_traits>
+
 #include "dg_device.h"
 #include "dg_internal.h"
 
@@ -100,6 +103,17 @@ __device__ __forceinline__ v8i make_v8i(uint4 lo, uint4 hi) {
   return r;
 }
 
+// Compile-time loop: f(std::integral_constant<int, 0>) ... f(<N-1>).
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, N>(f); }
+
 __device__ __forceinline__ v4f mfma_fp8_slice(const v8i& a, const v8i& b) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
   // Format codes 0/0 = e4m3 for both operands; no block scale (the scales here
@@ -124,6 +138,15 @@ struct Tile {
   static constexpr int kLPW = kAJ + kBJ;            // A/B DMAs per wave per stage; waves 0
                                                     // and 1 issue one more each, for the
                                                     // activation and the weight scales
+  static constexpr int kIssue = kLPW + 1;           // DMA pieces per wave per stage
+  // Fragment rows over which a stage's DMA pieces are spread (0: all of
+  // them right after the barrier, before any compute).  Spreading pays with
+  // two waves per SIMD, where the other wave keeps the SIMD busy while one
+  // waits on the address unit; with one wave per SIMD (4-wave tiles) issuing
+  // early measured faster.  The 256x256 tile sits at the 256-register limit
+  // of two waves per SIMD; keeping DMA addresses live across its rows would
+  // spill, so it issues everything after the first row's MFMAs.
+  static constexpr int kSpreadRows = kWaves < 8 ? 0 : ((BM * BN >= 256 * 256) ? 1 : FM);
   static constexpr int kSOffInstr = kAInstr + kBInstr;
   static constexpr int kSBOff = (kAInstr + kBInstr + 1) * 1024;  // weight scales of the slice
   static constexpr int kStageBytes = (kAInstr + kBInstr + 2) * 1024;
@@ -266,42 +289,70 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
       const uint8_t* B = uniform_ptr(p.b + (int64_t)g * p.b_gstride);
       const float* SB = uniform_ptr(p.sfb + (int64_t)g * p.sfb_gstride);
       const int nkb = kb1 - kb0;
+      // K walk order.  With k_rotate the tile visits its slices starting at
+      // (tile mod slices) and wraps, so workgroups running at the same time
+      // read different 128-byte columns of B.  When every tile starts at the
+      // same slice, the concurrent requests differ only in their row bits,
+      // and for power-of-two row pitches they crowd onto a few HBM channels
+      // (measured: 3.7 TB/s streaming rows 16 KiB apart, 5.7 TB/s rotated).
+      const int rot = (s.k_rotate && nkb > 1) ? t % nkb : 0;
+      auto kb_at = [&](int it) {
+        const int x = it + rot;
+        return kb0 + (x >= nkb ? x - nkb : x);
+      };
 
       const int cb_first = n0 >> 7;  // the tile's 128-column weight-scale blocks
       const int cb_count = min((n0 + T::BN - 1) >> 7, n_blocks - 1) - cb_first + 1;
 
       // Stage loader.  DMA instruction i of a stage fills LDS bytes
       // [1024 i, 1024 i + 1024): instructions [0, BM/8) carry A rows,
-      // [BM/8, (BM+BN)/8) B rows, then the BM activation scales, then padding
-      // so that every wave issues exactly kLPW instructions per stage.
-      auto issue_stage = [&](int kb, int buf) {
+      // [BM/8, (BM+BN)/8) B rows, then the BM activation scales and the
+      // weight scales.  A wave's share of a stage is kLPW A/B instructions
+      // plus, for waves 0 and 1, one scale instruction: piece j of
+      // kIssue = kLPW + 1 (a compile-time index; the last piece is the scale
+      // DMA, empty for waves 2 and up).
+      auto issue_piece = [&](int kb, int buf, auto jc) {
+        constexpr int j = decltype(jc)::value;
         const uint32_t stage_lds = smem_base + buf * T::kStageBytes;
-#pragma unroll
-        for (int j = 0; j < T::kAJ; ++j) {
+        if constexpr (j < T::kAJ) {
           const int instr = j * T::kWaves + wave;
           const int q = instr * 64 + lane;
           const int r = q >> 3, c = (q & 7) ^ (r & 7);
           const int gr = min(m0 + r, rows_valid - 1);
           dma16(stage_lds + instr * 1024, A, (uint32_t)gr * (uint32_t)p.lda + kb * 128 + c * 16);
-        }
-#pragma unroll
-        for (int j = 0; j < T::kBJ; ++j) {
-          const int instr = (T::kAJ + j) * T::kWaves + wave;
-          const int q = (j * T::kWaves + wave) * 64 + lane;
+        } else if constexpr (j < T::kLPW) {
+          constexpr int jb = j - T::kAJ;
+          const int instr = (T::kAJ + jb) * T::kWaves + wave;
+          const int q = (jb * T::kWaves + wave) * 64 + lane;
           const int r = q >> 3, c = (q & 7) ^ (r & 7);
           const int gn = min(n0 + r, p.n - 1);
           dma16(stage_lds + instr * 1024, B, (uint32_t)gn * (uint32_t)p.ldb + kb * 128 + c * 16);
+        } else {
+          if (wave == 0) {
+            // Activation scales of the slice: rows m0 .. m0 + 4*63 + 3.
+            const int r4 = min(m0 + 4 * lane, (int)p.ld_sfa - 4);
+            dma16(stage_lds + T::kSOffInstr * 1024, SA, (uint32_t)(kb * p.ld_sfa + r4) * 4u);
+          } else if (wave == 1) {
+            // Weight scales of the slice for the tile's column blocks (lane l:
+            // block cb_first + l; lanes past the last block repeat it).
+            const int cb = cb_first + min(lane, cb_count - 1);
+            dma4(stage_lds + T::kSBOff, SB, (uint32_t)(cb * nkb_total + kb) * 4u);
+          }
         }
-        if (wave == 0) {
-          // Activation scales of the slice: rows m0 .. m0 + 4*63 + 3.
-          const int r4 = min(m0 + 4 * lane, (int)p.ld_sfa - 4);
-          dma16(stage_lds + T::kSOffInstr * 1024, SA, (uint32_t)(kb * p.ld_sfa + r4) * 4u);
-        } else if (wave == 1) {
-          // Weight scales of the slice for the tile's column blocks (lane l:
-          // block cb_first + l; lanes past the last block repeat it).
-          const int cb = cb_first + min(lane, cb_count - 1);
-          dma4(stage_lds + T::kSBOff, SB, (uint32_t)(cb * nkb_total + kb) * 4u);
-        }
+      };
+      auto issue_stage = [&](int kb, int buf) {
+        static_for<T::kIssue>([&](auto jc) { issue_piece(kb, buf, jc); });
+      };
+      // The pieces that go out after the MFMAs of fragment row i, spreading a
+      // stage's DMAs over the compute of the previous one: the vector-memory
+      // address unit takes one 1 KB instruction per 16 clocks, so a wave that
+      // issued its whole share at once would sit idle behind the queue.
+      auto issue_row = [&](int kb, int buf, auto ic) {
+        constexpr int i = decltype(ic)::value;
+        static_for<T::kIssue>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          if constexpr (j * T::kSpreadRows / T::kIssue == i) issue_piece(kb, buf, jc);
+        });
       };
 
       lds_barrier();  // previous unit's readers are done with every LDS buffer
@@ -314,7 +365,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
 
 #pragma unroll
       for (int st = 0; st < T::STAGES - 1; ++st)
-        if (st < nkb) issue_stage(kb0 + st, st);
+        if (st < nkb) issue_stage(kb_at(st), st);
 
       for (int it = 0; it < nkb; ++it) {
         // Wait for this wave's DMAs of stage `it` (newer stages may stay in
@@ -326,7 +377,14 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
           wait_vm<0>();
         }
         barrier_all();
-        if (it + T::STAGES - 1 < nkb) issue_stage(kb0 + it + T::STAGES - 1, (it + T::STAGES - 1) % T::STAGES);
+        // Stage it + STAGES - 1 reuses the buffer of stage it - 1, which every
+        // wave finished reading before the barrier above.
+        const bool refill = it + T::STAGES - 1 < nkb;
+        const int kb_next = refill ? kb_at(it + T::STAGES - 1) : 0;
+        const int buf_next = (it + T::STAGES - 1) % T::STAGES;
+        if constexpr (T::kSpreadRows == 0) {
+          if (refill) issue_stage(kb_next, buf_next);
+        }
 
         const uint8_t* st = smem + (it % T::STAGES) * T::kStageBytes;
         float sbw = 0.0f;
@@ -367,20 +425,23 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
 #pragma unroll
           for (int j = 0; j < T::FN; ++j) part[0][j] = mfma_fp8_slice(afrag, bfrag[j]);
         }
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i) {
-          const int cur = T::kPipe ? (i & 1) : 0;
+        static_for<T::FM>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          constexpr int cur = T::kPipe ? (i & 1) : 0;
           const float4 s4 = load_s(i);
-          if (T::kPipe) {
-            if (i + 1 < T::FM) {
+          if constexpr (T::kPipe) {
+            if constexpr (i + 1 < T::FM) {
               afrag = load_a(i + 1);
 #pragma unroll
               for (int j = 0; j < T::FN; ++j) part[cur ^ 1][j] = mfma_fp8_slice(afrag, bfrag[j]);
             }
           } else {
-            if (i > 0) afrag = load_a(i);
+            if constexpr (i > 0) afrag = load_a(i);
 #pragma unroll
             for (int j = 0; j < T::FN; ++j) part[0][j] = mfma_fp8_slice(afrag, bfrag[j]);
+          }
+          if constexpr (T::kSpreadRows > 0) {
+            if (refill) issue_row(kb_next, buf_next, ic);
           }
           const float sa[4] = {s4.x, s4.y, s4.z, s4.w};
           float sc[4];
@@ -391,7 +452,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               acc[i][j][e] = fmaf(part[cur][j][e], T::kOneSB ? sc[e] : sa[e] * sbv[j], acc[i][j][e]);
-        }
+        });
       }
 
       // ------------------------------------------------------- split-K fixup
@@ -531,6 +592,8 @@ using TileW128 = Tile<128, 256, 2, 4, 3>;  // decode, M <= 128, wide N: 8 waves,
 using TileP128w8 = Tile<128, 128, 2, 4, 4>;  // decode: 8 waves (2 per SIMD), 64x32 per wave
 using TileS64w8 = Tile<64, 64, 2, 4, 8>;     // decode small tiles: 8 waves, 32x16 per wave
 using TileW128w16 = Tile<128, 256, 4, 4, 3>; // decode wide N: 16 waves, 32x64 per wave
+using TileV128 = Tile<128, 256, 1, 4, 3>;    // decode: every wave holds all 128 rows, 128x64 per wave
+using TileV128w8 = Tile<128, 256, 1, 8, 3>;  // the same with 8 waves, 128x32 per wave
 
 struct Variant {
   int bm, bn, threads;
@@ -545,6 +608,8 @@ constexpr Variant kVariants[] = {
     {TileP128w8::BM, TileP128w8::BN, TileP128w8::kThreads},
     {TileS64w8::BM, TileS64w8::BN, TileS64w8::kThreads},
     {TileW128w16::BM, TileW128w16::BN, TileW128w16::kThreads},
+    {TileV128::BM, TileV128::BN, TileV128::kThreads},
+    {TileV128w8::BM, TileV128w8::BN, TileV128w8::kThreads},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -584,20 +649,49 @@ int forced_split() {
   return c ? atoi(c + 1) : 0;
 }
 
+int forced_rotate() {  // third field: 0 or 1, -1 when absent
+  const char* e = getenv("DG_FORCE_CONFIG");
+  if (!e || !*e) return -1;
+  const char* c = strchr(e, ':');
+  if (!c) return -1;
+  c = strchr(c + 1, ':');
+  return c ? (atoi(c + 1) != 0) : -1;
+}
+
 }  // namespace
 
 GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cus) {
-  // m: dense M, contiguous M_total, masked M_max (expected rows are folded in
-  // by the caller through `groups` tiles; see below).
+  // m: dense M, contiguous M_total, masked M_max.  The rules below come from
+  // sweeps over tile variants and split counts on the benchmark shapes.
   const int nkb = k / kBlockK;
-  // Rows per group that the kernel will actually see.
   const int rows = m;
+  const int gmul = layout == kMasked ? groups : 1;
+  auto tiles_of = [&](int bm, int bn) { return cdiv(rows, bm) * gmul * cdiv(n, bn); };
+  auto fills = [&](int tiles) { return 10 * tiles >= 7 * num_cus; };  // >= 70% of the CUs
   int v;
-  if (rows <= 64) v = 3;
-  else if (rows <= 128) v = 1;
-  else {
-    const int t256 = cdiv(rows, 256) * cdiv(n, 256) * (layout == kMasked ? groups : 1);
+  int split = 1;
+  if (rows <= 128) {
+    // Decode-sized M: the launch streams B once; pick the tile that keeps
+    // the most CUs busy with the least A re-reading, then split K over the
+    // CUs the tiles leave idle.
+    const int t128 = tiles_of(128, 128), t64 = tiles_of(64, 64);
+    if (rows > 64 && (fills(t128) || nkb >= 64)) {
+      v = 6;  // 128x128, 8 waves
+      if (!fills(t128)) split = num_cus / t128;
+      split = std::min(split, nkb / 16);  // >= 16 slices per split
+    } else if (fills(t64)) {
+      v = 4;  // 64x64, 4 waves, 8 stages
+    } else {
+      v = 7;  // 64x64, 8 waves
+      split = std::min(std::min(4, num_cus / std::max(t64, 1)), nkb / 8);
+    }
+  } else {
+    const int t256 = tiles_of(256, 256);
     v = t256 >= num_cus / 2 ? 0 : 1;
+    if (v == 1) {
+      const int t = tiles_of(128, 128);
+      if (t < num_cus && nkb >= 8) split = std::min(num_cus / t, nkb / 4);
+    }
   }
   const int fv = forced_variant();
   if (fv >= 0 && fv < kNumVariants) v = fv;
@@ -605,34 +699,33 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
   c.variant = v;
   c.bm = kVariants[v].bm;
   c.bn = kVariants[v].bn;
-  const int m_tiles = cdiv(rows, c.bm) * (layout == kMasked ? groups : 1);
+  const int m_tiles = cdiv(rows, c.bm) * gmul;
   const int n_tiles = cdiv(n, c.bn);
   c.tiles = m_tiles * n_tiles;
-  // Split K when the tiles alone cannot fill the CUs, keeping >= 4 slices per
-  // split so the pipeline has something to overlap.
-  int split = 1;
-  if (c.tiles < num_cus && nkb >= 8) {
-    split = num_cus / c.tiles;
-    split = split < 1 ? 1 : split;
-    const int max_split = nkb / 4;
-    if (split > max_split) split = max_split;
-    if (split < 1) split = 1;
-  }
   const int fs = forced_split();
   if (fs > 0) split = fs < nkb ? fs : (nkb > 0 ? nkb : 1);
+  if (split < 1) split = 1;
   // A contiguous tile that straddles two experts runs two passes; split-K
   // bookkeeping assumes one pass per unit, so the contiguous layout never
   // splits (its M is large anyway).  Nor does the 256x256 tile (its
   // accumulators leave no registers for the reduction).
   if (nkb == 0 || layout == kContiguous || c.bm * c.bn >= 256 * 256) split = 1;
   c.split_k = split;
-  // Split-K: launch every unit (tiles * split <= CUs, so all valid units are
-  // resident together; units past the last tile exit at once).  Otherwise a
-  // persistent grid of at most one workgroup per CU.
+  // Split-K: launch every unit (with the rules above tiles * split <= CUs,
+  // so all valid units are resident together; units past the last tile exit
+  // at once).  Otherwise a persistent grid of at most one workgroup per CU.
   const int units = split > 1 ? cdiv(c.tiles, 8) * 8 * split : c.tiles;
   c.grid = split > 1 ? units : (units < num_cus ? units : num_cus);
   if (c.grid < 1) c.grid = 1;
   c.group_m = 8;
+  // Rotated K walks for the decode-sized tiles when the weight rows are a
+  // multiple of 16 KiB apart (see the kernel's K walk).  The 256x256 tile
+  // keeps every tile on the same slice: its operands are shared through L2
+  // by the tiles of a raster group, and rotation would spread that working
+  // set over many slices.
+  c.k_rotate = (c.bm * c.bn < 256 * 256 && k % 16384 == 0) ? 1 : 0;
+  const int fr = forced_rotate();
+  if (fr >= 0) c.k_rotate = fr;
   return c;
 }
 
@@ -656,6 +749,7 @@ hipError_t launch_gemm(int layout, const GemmParams& p0, const GemmConfig& cfg,
   s.tiles = cfg.tiles;
   s.units = cfg.split_k > 1 ? cdiv(cfg.tiles, 8) * 8 * cfg.split_k : cfg.tiles;
   s.group_m = cfg.group_m;
+  s.k_rotate = cfg.k_rotate;
   if (cfg.split_k > 1) {
     const size_t partial = (size_t)cfg.tiles * cfg.split_k * (size_t)cfg.bm * cfg.bn * sizeof(float);
     p.counters = reinterpret_cast<int*>(reinterpret_cast<char*>(p.workspace) + partial);
@@ -669,7 +763,9 @@ hipError_t launch_gemm(int layout, const GemmParams& p0, const GemmConfig& cfg,
     case 5: return launch_layout<TileW128>(layout, p, s, cfg.grid, stream);
     case 6: return launch_layout<TileP128w8>(layout, p, s, cfg.grid, stream);
     case 7: return launch_layout<TileS64w8>(layout, p, s, cfg.grid, stream);
-    default: return launch_layout<TileW128w16>(layout, p, s, cfg.grid, stream);
+    case 8: return launch_layout<TileW128w16>(layout, p, s, cfg.grid, stream);
+    case 9: return launch_layout<TileV128>(layout, p, s, cfg.grid, stream);
+    default: return launch_layout<TileV128w8>(layout, p, s, cfg.grid, stream);
   }
 }
 

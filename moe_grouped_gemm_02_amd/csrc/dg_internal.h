@@ -36,6 +36,7 @@ struct GemmConfig {
   int grid;      // workgroups launched (persistent)
   int tiles;     // output tiles over all groups (masked: worst case)
   int group_m;   // raster group height in M tiles
+  int k_rotate;  // 1: each tile starts its K walk at slice (tile mod slices)
 };
 
 // What the device needs to walk the work units of one launch.
@@ -47,6 +48,7 @@ struct Schedule {
   int split_k;
   int kb_per_split;  // K slices per split
   int group_m;
+  int k_rotate;      // see GemmConfig
 };
 
 GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cus);
