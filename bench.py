@@ -137,12 +137,13 @@ class Prepared:
         self.bytes = algorithmic_bytes(self.m_valid, n, k, g)
         self.sf_bytes = scale_bytes(self.m_valid, n, k, g)
         layout_id = {"dense": 0, "contiguous": 1, "masked": 2}[wl.layout]
-        self.config = dg.dg_describe_config(layout_id, self.m_rows, n, k, g, dg.dg_get_num_cus())
-        # One kernel instance per (tile variant, layout, split or not): the
+        self.expected_m = self.m_valid // g if wl.layout == "masked" else 0
+        self.config = dg.dg_describe_config(layout_id, self.m_rows, n, k, g, dg.dg_get_num_cus(), self.expected_m)
+        # One kernel instance per (tile variant, layout, stream-K or not): the
         # unit rocprofv3 reports durations for.
         fields = dict(kv.split("=") for kv in self.config.split())
         self.kernel_key = (f"gemm_kernel variant={fields['variant']} bm={fields['bm']} bn={fields['bn']} "
-                           f"layout={wl.layout} split={'yes' if int(fields['split_k']) > 1 else 'no'}")
+                           f"layout={wl.layout} stream_k={fields['stream_k']}")
 
     def quant(self, dg):
         dg.dg_quant_1x128(self.x, self.a, self.sfa)
@@ -154,7 +155,7 @@ class Prepared:
         elif self.wl.layout == "contiguous":
             dg.dg_grouped_contiguous(self.a, self.sfa, b, sfb, self.d, self.mi, workspace=self.ws)
         else:
-            dg.dg_grouped_masked(self.a, self.sfa, b, sfb, self.d, self.mm, expected_m=self.m_valid // self.wl.groups,
+            dg.dg_grouped_masked(self.a, self.sfa, b, sfb, self.d, self.mm, expected_m=self.expected_m,
                                  workspace=self.ws)
 
 

@@ -160,7 +160,7 @@ size_t dg_get_workspace_size(int m, int n, int k, int num_groups);
  * get_num_sms; project introduction, section Utility functions).  The default
  * is the device's CU count, or DG_NUM_CUS from the environment.
  * dg_get_num_cus returns a negative dg_status if no device can be queried;
- * dg_set_num_cus(0) restores the default. */
+ * dg_set_num_cus accepts 0 .. 4096, 0 restoring the default. */
 int dg_get_num_cus(void);
 int dg_set_num_cus(int num_cus);
 
@@ -177,11 +177,12 @@ int64_t dg_get_sf_leading_dim(int m);
 const char* dg_get_last_error_string(void);
 
 /* Human-readable description of the tile configuration the library would
- * choose for a GEMM (layout 0 = dense, 1 = contiguous, 2 = masked), written
- * into buf (NUL-terminated, truncated to len).  Returns DG_SUCCESS or an
- * error for invalid arguments.  Pure host logic: needs no device. */
-int dg_describe_config(int layout, int m, int n, int k, int num_groups, int num_cus,
-                       char* buf, size_t len);
+ * choose for a GEMM (layout 0 = dense, 1 = contiguous, 2 = masked; m is M,
+ * M_total or M_max; expected_m is the masked layout's hint, 0 otherwise),
+ * written into buf (NUL-terminated, truncated to len).  Returns DG_SUCCESS or
+ * an error for invalid arguments.  Pure host logic: needs no device. */
+int dg_describe_config(int layout, int m, int n, int k, int num_groups, int expected_m,
+                       int num_cus, char* buf, size_t len);
 
 #ifdef __cplusplus
 }

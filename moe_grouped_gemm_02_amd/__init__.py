@@ -41,7 +41,7 @@ _SIGNATURES = {
     "dg_get_m_alignment_for_contiguous_layout": (_I, []),
     "dg_get_sf_leading_dim": (_L, [_I]),
     "dg_get_last_error_string": (ctypes.c_char_p, []),
-    "dg_describe_config": (_I, [_I, _I, _I, _I, _I, _I, ctypes.c_char_p, _S]),
+    "dg_describe_config": (_I, [_I, _I, _I, _I, _I, _I, _I, ctypes.c_char_p, _S]),
 }
 for _name, (_res, _args) in _SIGNATURES.items():
     _fn = getattr(_lib, _name)
@@ -229,9 +229,9 @@ def dg_get_last_error_string():
     return _lib.dg_get_last_error_string().decode()
 
 
-def dg_describe_config(layout, m, n, k, num_groups=1, num_cus=256):
+def dg_describe_config(layout, m, n, k, num_groups=1, num_cus=256, expected_m=0):
     buf = ctypes.create_string_buffer(256)
-    _check("dg_describe_config", _lib.dg_describe_config(layout, m, n, k, num_groups, num_cus, buf, 256))
+    _check("dg_describe_config", _lib.dg_describe_config(layout, m, n, k, num_groups, expected_m, num_cus, buf, 256))
     return buf.value.decode()
 
 

@@ -37,7 +37,7 @@ int env_num_cus() {
   const char* s = getenv("DG_NUM_CUS");
   if (!s || !*s) return 0;
   const int v = atoi(s);
-  return v > 0 ? v : 0;
+  return v > 0 ? (v < 4096 ? v : 4096) : 0;
 }
 
 // CU count the persistent schedule is sized to; negative on failure.
@@ -100,17 +100,17 @@ int check_workspace(const dg::GemmConfig& cfg, int layout, int rows, int n, int 
 }
 
 int run_gemm(int layout, dg::GemmParams& p, int rows, int groups, void* ws, size_t ws_bytes,
-             void* stream) {
+             void* stream, int expected_m = 0) {
   const int cus = resolve_num_cus();
   if (cus < 0) return fail(DG_ERR_HIP, "cannot query the device's compute-unit count");
-  const dg::GemmConfig cfg = dg::choose_config(layout, rows, p.n, p.k, groups, cus);
+  const dg::GemmConfig cfg = dg::choose_config(layout, rows, p.n, p.k, groups, cus, expected_m);
   int st = check_workspace(cfg, layout, rows, p.n, groups, ws, ws_bytes);
   if (st != DG_SUCCESS) return st;
   p.workspace = static_cast<float*>(ws);
   p.counters = nullptr;
   if (debug_enabled())
-    fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d: bm=%d bn=%d split_k=%d grid=%d tiles=%d variant=%d cus=%d\n",
-            layout_name(layout), rows, p.n, p.k, groups, cfg.bm, cfg.bn, cfg.split_k, cfg.grid,
+    fprintf(stderr, "[dg] %s m=%d n=%d k=%d groups=%d: bm=%d bn=%d stream_k=%d grid=%d tiles=%d variant=%d cus=%d\n",
+            layout_name(layout), rows, p.n, p.k, groups, cfg.bm, cfg.bn, cfg.stream_k, cfg.grid,
             cfg.tiles, cfg.variant, cus);
   const hipError_t e = dg::launch_gemm(layout, p, cfg, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_HIP, "GEMM launch failed: %s", hipGetErrorString(e));
@@ -175,7 +175,7 @@ int dg_grouped_masked(const uint8_t* a, const float* sfa, const uint8_t* b, cons
   p.b_gstride = (int64_t)n * k;
   p.sfb_gstride = (int64_t)((n + 127) / 128) * (k / 128);
   p.d_gstride = (int64_t)m_max * n;
-  return run_gemm(dg::kMasked, p, m_max, num_groups, workspace, workspace_bytes, stream);
+  return run_gemm(dg::kMasked, p, m_max, num_groups, workspace, workspace_bytes, stream, expected_m);
 }
 
 int dg_quant_1x128(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
@@ -211,12 +211,17 @@ size_t dg_get_workspace_size(int m, int n, int k, int num_groups) {
   if (m <= 0 || n <= 0 || k <= 0 || num_groups < 1) return 0;
   int cus = resolve_num_cus();
   if (cus < 0) cus = 256;
+  // The largest need over the layouts and, for the masked layout, over the
+  // tile shapes its expected_m hint can select.
   size_t worst = 0;
-  for (int layout = dg::kDense; layout <= dg::kMasked; ++layout) {
-    const dg::GemmConfig c = dg::choose_config(layout, m, n, k, num_groups, cus);
-    const size_t need = dg::workspace_bytes_for(c, layout, m, n, num_groups);
-    if (need > worst) worst = need;
-  }
+  const int hints[] = {0, 1, 64, 65, 128, 129, 256, 257};
+  for (int layout = dg::kDense; layout <= dg::kMasked; ++layout)
+    for (int h : hints) {
+      if (h && layout != dg::kMasked) break;
+      const dg::GemmConfig c = dg::choose_config(layout, m, n, k, num_groups, cus, h);
+      const size_t need = dg::workspace_bytes_for(c, layout, m, n, num_groups);
+      if (need > worst) worst = need;
+    }
   return worst;
 }
 
@@ -227,7 +232,7 @@ int dg_get_num_cus(void) {
 }
 
 int dg_set_num_cus(int num_cus) {
-  if (num_cus < 0) return fail(DG_ERR_INVALID_VALUE, "num_cus must be >= 0");
+  if (num_cus < 0 || num_cus > 4096) return fail(DG_ERR_INVALID_VALUE, "num_cus must be in [0, 4096]");
   g_num_cus_override.store(num_cus);
   return ok();
 }
@@ -241,14 +246,14 @@ int64_t dg_get_sf_leading_dim(int m) {
 
 const char* dg_get_last_error_string(void) { return g_last_error; }
 
-int dg_describe_config(int layout, int m, int n, int k, int num_groups, int num_cus, char* buf,
-                       size_t len) {
+int dg_describe_config(int layout, int m, int n, int k, int num_groups, int expected_m,
+                       int num_cus, char* buf, size_t len) {
   if (layout < dg::kDense || layout > dg::kMasked || m < 0 || n < 0 || k < 0 ||
-      num_groups < 1 || num_cus < 1 || !buf || len == 0)
+      num_groups < 1 || expected_m < 0 || num_cus < 1 || !buf || len == 0)
     return fail(DG_ERR_INVALID_VALUE, "bad arguments to dg_describe_config");
-  const dg::GemmConfig c = dg::choose_config(layout, m, n, k, num_groups, num_cus);
-  snprintf(buf, len, "layout=%s bm=%d bn=%d split_k=%d grid=%d tiles=%d variant=%d k_rotate=%d workspace=%zu",
-           layout_name(layout), c.bm, c.bn, c.split_k, c.grid, c.tiles, c.variant, c.k_rotate,
+  const dg::GemmConfig c = dg::choose_config(layout, m, n, k, num_groups, num_cus, expected_m);
+  snprintf(buf, len, "layout=%s bm=%d bn=%d stream_k=%d sk_split=%d grid=%d tiles=%d variant=%d k_rotate=%d workspace=%zu",
+           layout_name(layout), c.bm, c.bn, c.stream_k, c.sk_split, c.grid, c.tiles, c.variant, c.k_rotate,
            dg::workspace_bytes_for(c, layout, m, n, num_groups));
   return ok();
 }

@@ -29,8 +29,9 @@
 // * Split-K (for shapes with fewer tiles than CUs): each unit computes a K
 //   range of one tile and writes an fp32 partial; the last unit of a tile to
 //   finish (arrival counter) sums the partials in split order - a fixed order,
-//   so results are bit-identical run to run - and stores bf16.  The splits of
-//   a tile are placed on one XCD so the partials stay in its L2.
+//   so results are bit-identical run to run - and stores bf16.  Each XCD is
+//   given the tiles of one K range, so the activation slices of that range,
+//   which every tile reads, stay in the XCD's L2.
 //
 // The unaligned tile widths (BN not a power of two) follow the pages' point
 // that power-of-two blocks can leave SMs idle (project introduction,
@@ -189,7 +190,7 @@ __device__ __forceinline__ void raster(int t, int m_tiles, int n_tiles, int grou
 
 __device__ __forceinline__ int clamp_rows(int v, int hi) { return v < 0 ? 0 : (v > hi ? hi : v); }
 
-template <class T, int LAYOUT, bool SPLIT>
+template <class T, int LAYOUT, bool SK>
 __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedule s) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::STAGES * T::kStageBytes];
   __shared__ int last_flag;
@@ -213,21 +214,71 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
       m_tiles += (clamp_rows(p.masked_m[g], p.m) + T::BM - 1) / T::BM;
   }
   const int tiles = m_tiles * s.n_tiles;
-  const int units = SPLIT ? ((tiles + 7) / 8) * 8 * s.split_k : tiles;
+  const int G = gridDim.x;
+  // Stream-K.  The tiles of the whole waves of G run one per workgroup
+  // (data-parallel); the (tile, K slice) iterations of the remaining tiles
+  // are divided into runs, each a contiguous range of iterations:
+  //   sk_split == 0: sk_groups = min(G, iterations) runs of equal length,
+  //     which may cross tile boundaries (long K ranges, few tiles);
+  //   sk_split == S: S runs per tile, each 1/S of its K range (one
+  //     segment per run; runs beyond G go round again).
+  // A run that covers only part of a tile's K range leaves an fp32 partial;
+  // the last workgroup of that tile to finish sums the partials in K order.
+  const int sk_split = min(s.sk_split, nkb_total);  // no empty runs
+  int dp_tiles = tiles, sk_iters = 0, sk_groups = 1;
+  if (SK) {
+    dp_tiles = sk_split > 0 ? 0 : (tiles / G) * G;
+    sk_iters = (tiles - dp_tiles) * nkb_total;
+    sk_groups = sk_split > 0 ? (tiles - dp_tiles) * sk_split : max(1, min(G, sk_iters));
+  }
+  auto sk_start = [&](int w) {
+    if (sk_split > 0) {
+      const int tt = w / sk_split;
+      return tt * nkb_total + ((w - tt * sk_split) * nkb_total) / sk_split;
+    }
+    return (int)(((int64_t)sk_iters * w) / sk_groups);
+  };
+  auto sk_owner = [&](int x) {  // the run containing iteration x
+    int w = (int)(((int64_t)x * sk_groups) / sk_iters);
+    while (w + 1 < sk_groups && sk_start(w + 1) <= x) ++w;
+    while (w > 0 && sk_start(w) > x) --w;
+    return w;
+  };
+  // Runs are numbered so that the workgroups of one XCD (id mod 8) take
+  // neighbouring runs, i.e. neighbouring tiles.
+  const int vw = (SK && (G & 7) == 0) ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  int run = vw, sk_cur = 0, sk_end = 0, run_first = 0;
+  if (SK && run < sk_groups) {
+    sk_cur = run_first = sk_start(run);
+    sk_end = sk_start(run + 1);
+  }
+  int dp_u = blockIdx.x;
 
-  for (int u = blockIdx.x; u < units; u += gridDim.x) {
+  while (true) {
     // ------------------------------------------------------------ schedule
-    int t, split = 0;
-    if (SPLIT) {
-      // Units are ordered so that the splits of one tile are 8 apart, i.e. on
-      // the same XCD: u = (tile / 8) * 8 * S + split * 8 + tile % 8.
-      const int blk = u / (8 * s.split_k);
-      const int r = u - blk * 8 * s.split_k;
-      split = r >> 3;
-      t = blk * 8 + (r & 7);
-      if (t >= tiles) continue;
+    int t, kb0, kb1;
+    bool partial = false;  // this unit computes part of the tile's K range
+    int slot = 0;          // 0: the run's first segment, 1: its last
+    if (SK && sk_cur >= sk_end && sk_split > 0 && run + G < sk_groups) {
+      run += G;  // aligned runs beyond the grid go round again
+      sk_cur = run_first = sk_start(run);
+      sk_end = sk_start(run + 1);
+    }
+    if (sk_cur < sk_end) {
+      const int tr = sk_cur / nkb_total;
+      kb0 = sk_cur - tr * nkb_total;
+      kb1 = min(nkb_total, kb0 + (sk_end - sk_cur));
+      slot = sk_cur == run_first ? 0 : 1;
+      sk_cur += kb1 - kb0;
+      t = dp_tiles + tr;
+      partial = !(kb0 == 0 && kb1 == nkb_total);
+    } else if (dp_u < dp_tiles) {
+      t = xcd_remap(dp_u, G, dp_tiles);
+      kb0 = 0;
+      kb1 = nkb_total;
+      dp_u += G;
     } else {
-      t = xcd_remap(u, gridDim.x, units);
+      break;
     }
     int mt, nt;
     raster(t, m_tiles, s.n_tiles, s.group_m, mt, nt);
@@ -243,8 +294,6 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
     }
     const int m0 = mt * T::BM;
     const int n0 = nt * T::BN;
-    const int kb0 = split * s.kb_per_split;
-    const int kb1 = min(nkb_total, kb0 + s.kb_per_split);
 
     int rows_valid = p.m;
     const uint8_t* A = p.a;
@@ -421,6 +470,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
         };
         v4f part[T::kPipe ? 2 : 1][T::FN];
         v8i afrag = load_a(0);
+        float4 s4 = load_s(0);
         if (T::kPipe) {
 #pragma unroll
           for (int j = 0; j < T::FN; ++j) part[0][j] = mfma_fp8_slice(afrag, bfrag[j]);
@@ -428,22 +478,28 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
         static_for<T::FM>([&](auto ic) {
           constexpr int i = decltype(ic)::value;
           constexpr int cur = T::kPipe ? (i & 1) : 0;
-          const float4 s4 = load_s(i);
+          const float4 s_cur = s4;
           if constexpr (T::kPipe) {
             if constexpr (i + 1 < T::FM) {
               afrag = load_a(i + 1);
+              s4 = load_s(i + 1);
 #pragma unroll
               for (int j = 0; j < T::FN; ++j) part[cur ^ 1][j] = mfma_fp8_slice(afrag, bfrag[j]);
             }
           } else {
-            if constexpr (i > 0) afrag = load_a(i);
+            // MFMAs of row i, then the LDS reads of row i + 1, which complete
+            // while the promotion FMAs of row i run.
 #pragma unroll
             for (int j = 0; j < T::FN; ++j) part[0][j] = mfma_fp8_slice(afrag, bfrag[j]);
+            if constexpr (i + 1 < T::FM) {
+              afrag = load_a(i + 1);
+              s4 = load_s(i + 1);
+            }
           }
           if constexpr (T::kSpreadRows > 0) {
             if (refill) issue_row(kb_next, buf_next, ic);
           }
-          const float sa[4] = {s4.x, s4.y, s4.z, s4.w};
+          const float sa[4] = {s_cur.x, s_cur.y, s_cur.z, s_cur.w};
           float sc[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) sc[e] = T::kOneSB ? sa[e] * sbw : 0.0f;
@@ -456,65 +512,65 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
       }
 
       // ------------------------------------------------------- split-K fixup
-      if (SPLIT && s.split_k > 1) {
-        // Partials go through agent-scope (sc1) stores and loads, which are
-        // coherent across XCDs without a cache-wide write-back.  Each thread
-        // waits for its stores to complete before the barrier; the arrival
-        // counter is bumped after the barrier, so a unit that sees the count
-        // reach split_k - 1 reads complete partials.
-        uint64_t* ws = reinterpret_cast<uint64_t*>(p.workspace);
-        const int fr_per = T::FM * T::FN;
-        uint64_t* mine = ws + ((int64_t)(t * s.split_k + split) * fr_per) * T::kThreads * 2;
+      if (SK && partial) {
+        // Partials go through device-scope (sc1) 16-byte buffer stores and
+        // loads, which are coherent across XCDs without a cache-wide
+        // write-back.  Each thread waits for its stores to complete before the
+        // barrier; the arrival counter is bumped after the barrier, so the
+        // workgroup that sees the count reach (contributors - 1) reads
+        // complete partials.  Slot 2 r + {0, 1} holds run r's first / last
+        // segment; a slot is [fragment][thread] float4.
+        constexpr int kFrag = T::FM * T::FN;
+        constexpr int kPartBytes = kFrag * T::kThreads * 16;  // BM * BN * 4
+        constexpr int kCacheSc1 = 16;                         // cache-policy bits: sc1
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            uniform_ptr(p.workspace), (short)0, 2 * s.sk_slots * kPartBytes, 0x00020000);
+        const int my_slot = 2 * run + slot;
 #pragma unroll
-        for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < T::FN; ++j) {
-            uint64_t* dst = mine + ((i * T::FN + j) * T::kThreads + tid) * 2;
-            const uint64_t lo = ((uint64_t)__float_as_uint(acc[i][j][1]) << 32) | __float_as_uint(acc[i][j][0]);
-            const uint64_t hi = ((uint64_t)__float_as_uint(acc[i][j][3]) << 32) | __float_as_uint(acc[i][j][2]);
-            __hip_atomic_store(dst, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(dst + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
+        for (int f = 0; f < kFrag; ++f)
+          __builtin_amdgcn_raw_buffer_store_b128(acc[f / T::FN][f % T::FN], rs,
+                                                 my_slot * kPartBytes + f * T::kThreads * 16 + tid * 16, 0, kCacheSc1);
         asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
         __syncthreads();
+        const int tr = t - dp_tiles;
+        const int it_a = tr * nkb_total;
+        const int w_lo = sk_owner(it_a), w_hi = sk_owner(it_a + nkb_total - 1);
         if (tid == 0) {
           const int old = __hip_atomic_fetch_add(&p.counters[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          last_flag = (old == s.split_k - 1);
+          last_flag = (old == w_hi - w_lo);
         }
         __syncthreads();
         if (!last_flag) continue;
-        // Sum every split's partial, this unit's own included, in split order.
+        // Sum the partials of runs w_lo .. w_hi (ascending K) into acc, in
+        // chunks of fragments with up to kG runs' loads in flight.
+        const int lo_slot = sk_start(w_lo) < it_a ? 1 : 0;  // run w_lo began in an earlier tile
+        constexpr int kChunk = kFrag < 8 ? kFrag : 8;
+        constexpr int kG = T::kWaves >= 16 ? 1 : (kFrag >= 32 ? 2 : 4);
+        static_assert(kFrag % kChunk == 0, "fragments must split into whole chunks");
+        static_for<kFrag / kChunk>([&](auto cc) {
+          constexpr int f0 = decltype(cc)::value * kChunk;
 #pragma unroll
-        for (int i = 0; i < T::FM; ++i)
+          for (int f = 0; f < kChunk; ++f) acc[(f0 + f) / T::FN][(f0 + f) % T::FN] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+          for (int w = w_lo; w <= w_hi; w += kG) {
+            v4f v[kG][kChunk];
 #pragma unroll
-          for (int j = 0; j < T::FN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        for (int sp = 0; sp < s.split_k; sp += 2) {
-          // Two splits' loads in flight at once; summed in split order.
-          const bool two = sp + 1 < s.split_k;
-          uint64_t* src0 = ws + ((int64_t)(t * s.split_k + sp) * fr_per) * T::kThreads * 2;
-          uint64_t* src1 = two ? src0 + (int64_t)fr_per * T::kThreads * 2 : src0;
-          uint64_t v0[T::FM][T::FN][2], v1[T::FM][T::FN][2];
+            for (int q = 0; q < kG; ++q) {
+              const int src = 2 * (w + q) + ((w + q) == w_lo ? lo_slot : 0);
 #pragma unroll
-          for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-            for (int j = 0; j < T::FN; ++j) {
-              const int64_t e = ((i * T::FN + j) * T::kThreads + tid) * 2;
-              v0[i][j][0] = __hip_atomic_load(src0 + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              v0[i][j][1] = __hip_atomic_load(src0 + e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              v1[i][j][0] = __hip_atomic_load(src1 + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              v1[i][j][1] = __hip_atomic_load(src1 + e + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              for (int f = 0; f < kChunk; ++f)
+                v[q][f] = w + q <= w_hi
+                              ? __builtin_amdgcn_raw_buffer_load_b128(
+                                    rs, src * kPartBytes + (f0 + f) * T::kThreads * 16 + tid * 16, 0, kCacheSc1)
+                              : v4f{0.0f, 0.0f, 0.0f, 0.0f};
             }
 #pragma unroll
-          for (int i = 0; i < T::FM; ++i)
+            for (int q = 0; q < kG; ++q)
+              if (w + q <= w_hi) {
 #pragma unroll
-            for (int j = 0; j < T::FN; ++j) {
-              acc[i][j] += v4f{__uint_as_float((uint32_t)v0[i][j][0]), __uint_as_float((uint32_t)(v0[i][j][0] >> 32)),
-                               __uint_as_float((uint32_t)v0[i][j][1]), __uint_as_float((uint32_t)(v0[i][j][1] >> 32))};
-              if (two)
-                acc[i][j] += v4f{__uint_as_float((uint32_t)v1[i][j][0]), __uint_as_float((uint32_t)(v1[i][j][0] >> 32)),
-                                 __uint_as_float((uint32_t)v1[i][j][1]), __uint_as_float((uint32_t)(v1[i][j][1] >> 32))};
-            }
-        }
+                for (int f = 0; f < kChunk; ++f) acc[(f0 + f) / T::FN][(f0 + f) % T::FN] += v[q][f];
+              }
+          }
+        });
         if (tid == 0) __hip_atomic_store(&p.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
 
@@ -587,10 +643,10 @@ using TileP256 = Tile<256, 256, 2, 4, 2>;  // prefill: 8 waves, 128x64 per wave
 using TileP128 = Tile<128, 128, 2, 2, 4>;  // mid-size and decode M <= 128: 64x64 per wave
 using TileD128 = Tile<128, 64, 2, 2, 4>;   // decode, narrow N tiles: 64x32 per wave
 using TileD64 = Tile<64, 256, 1, 4, 3>;    // decode, M <= 64: 64x64 per wave
-using TileS64 = Tile<64, 64, 2, 2, 8>;     // decode, small tiles, deep pipeline: 32x32 per wave
+using TileS64 = Tile<64, 64, 2, 2, 4>;     // decode, small tiles: 32x32 per wave
 using TileW128 = Tile<128, 256, 2, 4, 3>;  // decode, M <= 128, wide N: 8 waves, 64x64 per wave
 using TileP128w8 = Tile<128, 128, 2, 4, 4>;  // decode: 8 waves (2 per SIMD), 64x32 per wave
-using TileS64w8 = Tile<64, 64, 2, 4, 8>;     // decode small tiles: 8 waves, 32x16 per wave
+using TileS64w8 = Tile<64, 64, 2, 4, 4>;     // decode small tiles: 8 waves, 32x16 per wave
 using TileW128w16 = Tile<128, 256, 4, 4, 3>; // decode wide N: 16 waves, 32x64 per wave
 using TileV128 = Tile<128, 256, 1, 4, 3>;    // decode: every wave holds all 128 rows, 128x64 per wave
 using TileV128w8 = Tile<128, 256, 1, 8, 3>;  // the same with 8 waves, 128x32 per wave
@@ -615,8 +671,8 @@ constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 template <class T, int LAYOUT>
 hipError_t launch_one(const GemmParams& p, const Schedule& s, int grid, hipStream_t stream) {
-  if constexpr (T::BM * T::BN < 256 * 256) {  // the 256x256 tile never splits
-    if (s.split_k > 1) {
+  if constexpr (LAYOUT != kContiguous) {  // contiguous tiles may take two passes: data-parallel only
+    if (s.stream_k) {
       hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
       return hipGetLastError();
     }
@@ -636,17 +692,24 @@ hipError_t launch_layout(int layout, const GemmParams& p, const Schedule& s, int
 
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Stream-K partial slots are addressed with 32-bit offsets: 2 * grid slots of
+// at most 256 KB stay below 2^31 bytes with this cap.
+constexpr int kMaxStreamKGrid = 1024;
+
 int forced_variant() {
-  const char* e = getenv("DG_FORCE_CONFIG");  // "variant:split_k", for sweeps
+  // DG_FORCE_CONFIG="variant[:division[:k_rotate]]" overrides the heuristic
+  // (sweeps and tests); division 0 = data-parallel, 1 = equal stream-K runs,
+  // S >= 2 = S parts per tile.
+  const char* e = getenv("DG_FORCE_CONFIG");
   if (!e || !*e) return -1;
   return atoi(e);
 }
 
-int forced_split() {
+int forced_stream_k() {  // second field, -1 when absent
   const char* e = getenv("DG_FORCE_CONFIG");
-  if (!e || !*e) return 0;
+  if (!e || !*e) return -1;
   const char* c = strchr(e, ':');
-  return c ? atoi(c + 1) : 0;
+  return c ? std::max(0, atoi(c + 1)) : -1;
 }
 
 int forced_rotate() {  // third field: 0 or 1, -1 when absent
@@ -660,38 +723,25 @@ int forced_rotate() {  // third field: 0 or 1, -1 when absent
 
 }  // namespace
 
-GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cus) {
+GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cus, int expected_m) {
   // m: dense M, contiguous M_total, masked M_max.  The rules below come from
-  // sweeps over tile variants and split counts on the benchmark shapes.
+  // sweeps over tile variants on the benchmark shapes.  For the masked
+  // layout a host hint of the typical valid rows per group replaces M_max in
+  // the choice of tile (the launch itself still covers M_max rows per group,
+  // skipping empty tiles on the device).
   const int nkb = k / kBlockK;
-  const int rows = m;
+  const bool hinted = layout == kMasked && expected_m > 0 && expected_m < m;
+  const int rows = hinted ? expected_m : m;
   const int gmul = layout == kMasked ? groups : 1;
   auto tiles_of = [&](int bm, int bn) { return cdiv(rows, bm) * gmul * cdiv(n, bn); };
-  auto fills = [&](int tiles) { return 10 * tiles >= 7 * num_cus; };  // >= 70% of the CUs
   int v;
-  int split = 1;
   if (rows <= 128) {
-    // Decode-sized M: the launch streams B once; pick the tile that keeps
-    // the most CUs busy with the least A re-reading, then split K over the
-    // CUs the tiles leave idle.
-    const int t128 = tiles_of(128, 128), t64 = tiles_of(64, 64);
-    if (rows > 64 && (fills(t128) || nkb >= 64)) {
-      v = 6;  // 128x128, 8 waves
-      if (!fills(t128)) split = num_cus / t128;
-      split = std::min(split, nkb / 16);  // >= 16 slices per split
-    } else if (fills(t64)) {
-      v = 4;  // 64x64, 4 waves, 8 stages
-    } else {
-      v = 7;  // 64x64, 8 waves
-      split = std::min(std::min(4, num_cus / std::max(t64, 1)), nkb / 8);
-    }
+    // Decode-sized M: the launch streams B once.  128x128 tiles (8 waves)
+    // when they alone keep most CUs busy or K is long, else 64x64 tiles.
+    const int t128 = tiles_of(128, 128);
+    v = (rows > 64 && (10 * t128 >= 7 * num_cus || nkb >= 64)) ? 6 : 4;
   } else {
-    const int t256 = tiles_of(256, 256);
-    v = t256 >= num_cus / 2 ? 0 : 1;
-    if (v == 1) {
-      const int t = tiles_of(128, 128);
-      if (t < num_cus && nkb >= 8) split = std::min(num_cus / t, nkb / 4);
-    }
+    v = tiles_of(256, 256) >= num_cus / 2 ? 0 : 1;
   }
   const int fv = forced_variant();
   if (fv >= 0 && fv < kNumVariants) v = fv;
@@ -699,24 +749,41 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
   c.variant = v;
   c.bm = kVariants[v].bm;
   c.bn = kVariants[v].bn;
-  const int m_tiles = cdiv(rows, c.bm) * gmul;
+  const int m_tiles = cdiv(m, c.bm) * gmul;
   const int n_tiles = cdiv(n, c.bn);
   c.tiles = m_tiles * n_tiles;
-  const int fs = forced_split();
-  if (fs > 0) split = fs < nkb ? fs : (nkb > 0 ? nkb : 1);
-  if (split < 1) split = 1;
-  // A contiguous tile that straddles two experts runs two passes; split-K
-  // bookkeeping assumes one pass per unit, so the contiguous layout never
-  // splits (its M is large anyway).  Nor does the 256x256 tile (its
-  // accumulators leave no registers for the reduction).
-  if (nkb == 0 || layout == kContiguous || c.bm * c.bn >= 256 * 256) split = 1;
-  c.split_k = split;
-  // Split-K: launch every unit (with the rules above tiles * split <= CUs,
-  // so all valid units are resident together; units past the last tile exit
-  // at once).  Otherwise a persistent grid of at most one workgroup per CU.
-  const int units = split > 1 ? cdiv(c.tiles, 8) * 8 * split : c.tiles;
-  c.grid = split > 1 ? units : (units < num_cus ? units : num_cus);
-  if (c.grid < 1) c.grid = 1;
+  // Work division.  Tiles that leave most CUs idle get their K ranges cut:
+  // decode-sized tiles into S equal parts (one part per workgroup), larger
+  // tiles with long K into equal runs of iterations over all CUs.  The
+  // estimate uses the hinted rows for the masked layout.
+  const int est = tiles_of(c.bm, c.bn);
+  int sk = 0;  // 0: data-parallel, 1: equal runs, S >= 2: S parts per tile
+  if (layout != kContiguous && nkb >= 2 && 10 * est < 7 * num_cus) {
+    if (c.bm <= 128 && rows <= 128) {
+      const int min_slices = c.bm * c.bn >= 128 * 128 ? 16 : 8;
+      int parts = std::min(num_cus / std::max(est, 1), nkb / min_slices);
+      if (c.bm * c.bn < 128 * 128) parts = std::min(parts, 4);
+      if (parts >= 2) sk = parts;
+    } else if ((int64_t)est * nkb >= 24LL * num_cus) {
+      sk = 1;
+    }
+  }
+  const int fs = forced_stream_k();
+  if (fs >= 0) sk = fs;
+  if (layout == kContiguous || nkb < 2) sk = 0;
+  if (sk >= 2) sk = std::min(sk, nkb);
+  c.stream_k = sk > 0 ? 1 : 0;
+  c.sk_split = sk >= 2 ? sk : 0;
+  // Aligned parts: one workgroup per part, the grid a multiple of 8 so that
+  // the XCD-contiguous numbering of runs spreads them evenly over the XCDs.
+  const int cap = std::min(num_cus, kMaxStreamKGrid);
+  c.grid = !c.stream_k ? std::max(1, std::min(c.tiles, num_cus))
+           : (c.sk_split ? std::min(cap, cdiv(c.tiles * c.sk_split, 8) * 8) : cap);
+  c.sk_slots = c.sk_split ? c.tiles * c.sk_split : c.grid;
+  if (c.stream_k && (int64_t)2 * c.sk_slots * c.bm * c.bn * 4 >= (1LL << 31)) {
+    c.stream_k = c.sk_split = c.sk_slots = 0;  // partial slots must stay 32-bit addressable
+    c.grid = std::max(1, std::min(c.tiles, num_cus));
+  }
   c.group_m = 8;
   // Rotated K walks for the decode-sized tiles when the weight rows are a
   // multiple of 16 KiB apart (see the kernel's K walk).  The 256x256 tile
@@ -731,29 +798,26 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
 
 size_t workspace_bytes_for(const GemmConfig& cfg, int layout, int m, int n, int groups) {
   (void)layout; (void)m; (void)n; (void)groups;
-  if (cfg.split_k <= 1) return 0;
-  const size_t tiles = (size_t)cfg.tiles;
-  const size_t partial = tiles * cfg.split_k * (size_t)cfg.bm * cfg.bn * sizeof(float);
-  return partial + tiles * sizeof(int);
+  if (!cfg.stream_k) return 0;
+  // Two fp32 partial tiles per run, then one arrival counter per tile.
+  return 2 * (size_t)cfg.sk_slots * cfg.bm * cfg.bn * sizeof(float) + (size_t)cfg.tiles * sizeof(int);
 }
 
 hipError_t launch_gemm(int layout, const GemmParams& p0, const GemmConfig& cfg,
                        hipStream_t stream) {
   GemmParams p = p0;
-  const int nkb = p.k / kBlockK;
   Schedule s{};
-  s.split_k = cfg.split_k;
-  s.kb_per_split = cfg.split_k > 1 ? cdiv(nkb, cfg.split_k) : nkb;
   s.n_tiles = cdiv(p.n, cfg.bn);
   s.m_tiles = cfg.tiles / s.n_tiles;
   s.tiles = cfg.tiles;
-  s.units = cfg.split_k > 1 ? cdiv(cfg.tiles, 8) * 8 * cfg.split_k : cfg.tiles;
+  s.stream_k = cfg.stream_k;
+  s.sk_split = cfg.sk_split;
+  s.sk_slots = cfg.sk_slots;
   s.group_m = cfg.group_m;
   s.k_rotate = cfg.k_rotate;
-  if (cfg.split_k > 1) {
-    const size_t partial = (size_t)cfg.tiles * cfg.split_k * (size_t)cfg.bm * cfg.bn * sizeof(float);
-    p.counters = reinterpret_cast<int*>(reinterpret_cast<char*>(p.workspace) + partial);
-  }
+  if (cfg.stream_k)
+    p.counters = reinterpret_cast<int*>(reinterpret_cast<char*>(p.workspace) +
+                                        2 * (size_t)cfg.sk_slots * cfg.bm * cfg.bn * sizeof(float));
   switch (cfg.variant) {
     case 0: return launch_layout<TileP256>(layout, p, s, cfg.grid, stream);
     case 1: return launch_layout<TileP128>(layout, p, s, cfg.grid, stream);

@@ -17,8 +17,8 @@ struct GemmParams {
   uint16_t* d;
   const int32_t* m_indices;  // contiguous layout only
   const int32_t* masked_m;   // masked layout only
-  float* workspace;          // split-K partials (fp32), may be null
-  int* counters;             // split-K arrival counters, may be null
+  float* workspace;          // stream-K partials (fp32), may be null
+  int* counters;             // stream-K arrival counters, may be null
   int m;                     // dense: M; contiguous: M_total; masked: M_max
   int n;
   int k;
@@ -32,7 +32,9 @@ struct GemmConfig {
   int variant;   // kernel instance (tile shape), index into the kernel table
   int bm;
   int bn;
-  int split_k;   // number of K ranges per output tile (1 = none)
+  int stream_k;  // 1: K ranges of tiles divided among workgroups (stream-K)
+  int sk_split;  // 0: equal runs of iterations; S >= 2: S equal parts per tile
+  int sk_slots;  // runs with partial-result slots (2 slots each)
   int grid;      // workgroups launched (persistent)
   int tiles;     // output tiles over all groups (masked: worst case)
   int group_m;   // raster group height in M tiles
@@ -41,17 +43,19 @@ struct GemmConfig {
 
 // What the device needs to walk the work units of one launch.
 struct Schedule {
-  int units;         // tiles * split_k
   int tiles;
   int m_tiles;       // M tiles (masked: worst-case total over groups)
   int n_tiles;
-  int split_k;
-  int kb_per_split;  // K slices per split
+  int stream_k;
+  int sk_split;
+  int sk_slots;
   int group_m;
   int k_rotate;      // see GemmConfig
 };
 
-GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cus);
+// expected_m (masked layout only, 0 = unknown): typical valid rows per group,
+// used to pick the tile shape.
+GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cus, int expected_m = 0);
 size_t workspace_bytes_for(const GemmConfig& cfg, int layout, int m, int n, int groups);
 
 hipError_t launch_gemm(int layout, const GemmParams& p, const GemmConfig& cfg,

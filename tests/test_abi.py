@@ -105,10 +105,30 @@ def test_num_cus_override():
     dg.dg_set_num_cus(0)
     with pytest.raises(dg.DGError):
         dg.dg_set_num_cus(-1)
+    with pytest.raises(dg.DGError):
+        dg.dg_set_num_cus(4097)
+
+
+def test_stream_k_workspace_size():
+    # Decode-sized tiles: S equal K parts per tile, one workgroup per part (grid
+    # rounded up to a multiple of 8), two fp32 partial slots per part plus one
+    # arrival counter per tile.
+    for n, k in [(2112, 7168), (7168, 16384), (4096, 7168)]:
+        fields = dict(kv.split("=") for kv in dg.dg_describe_config(dg.LAYOUT_DENSE, 128, n, k, 1, 256).split())
+        grid, bm, bn, tiles, parts = (int(fields[x]) for x in ("grid", "bm", "bn", "tiles", "sk_split"))
+        assert int(fields["stream_k"]) == 1 and parts >= 2
+        assert grid == -(-tiles * parts // 8) * 8 <= 256
+        assert int(fields["workspace"]) == 2 * tiles * parts * bm * bn * 4 + tiles * 4
+    # Large tiles that fill under 70% of the CUs, long K: equal runs over all CUs.
+    fields = dict(kv.split("=") for kv in dg.dg_describe_config(dg.LAYOUT_DENSE, 4096, 2112, 7168, 1, 256).split())
+    assert int(fields["stream_k"]) == 1 and int(fields["sk_split"]) == 0 and int(fields["grid"]) == 256
+    assert int(fields["workspace"]) == 2 * 256 * 256 * 256 * 4 + int(fields["tiles"]) * 4
+    dense_full = dict(kv.split("=") for kv in dg.dg_describe_config(dg.LAYOUT_DENSE, 4096, 4096, 7168, 1, 256).split())
+    assert int(dense_full["tiles"]) == 256 and int(dense_full["stream_k"]) == 0 and int(dense_full["workspace"]) == 0
 
 
 def test_describe_config_is_host_only():
     s = dg.dg_describe_config(dg.LAYOUT_DENSE, 4096, 7168, 16384, 1, 256)
-    assert "bm=" in s and "bn=" in s and "split_k=" in s
+    assert "bm=" in s and "bn=" in s and "stream_k=" in s
     with pytest.raises(dg.DGError):
         dg.dg_describe_config(7, 1, 1, 128)

@@ -1,14 +1,19 @@
 """GPU parity of every kernel instance, not just the ones the tile heuristic
 picks for the shapes above.
 
-DG_FORCE_CONFIG="variant:split_k:k_rotate" overrides the heuristic (it is
-read on every call).  Each tile variant runs unsplit and with K split three
-ways, with the K walk rotated and not, on shapes that are ragged against
-every tile size (M = 150, N = 392) and whose K (12 slices) splits unevenly
-with rotation; the masked and contiguous layouts run the same sweep.  Every
-output element is compared with the oracle under the bf16 tolerance rule.
+DG_FORCE_CONFIG="variant:division:k_rotate" overrides the heuristic (it is
+read on every call); division 0 is data-parallel, 1 divides the tiles' K
+iterations into equal runs over the grid (stream-K), 3 cuts every tile's K
+range into 3 parts.  Each tile variant runs every division, with the K walk
+rotated and not, on shapes that are ragged against every tile size
+(M = 150, N = 392) with K = 12 slices; the masked and contiguous layouts run
+the same sweep.  Both stream-K divisions also run with grid sizes (the
+library's CU count) that cut the tiles' K ranges at many different places,
+including grids larger than the number of iterations, grids smaller than
+the number of parts and grids that are not a multiple of the XCD count.
+Every output element is compared with the oracle under the bf16 tolerance
+rule.
 """
-
 
 import numpy as np
 import pytest
@@ -27,10 +32,17 @@ M, N, K = 150, 392, 1536
 
 @pytest.fixture
 def force(monkeypatch):
-    def _set(variant, split, rotate):
-        monkeypatch.setenv("DG_FORCE_CONFIG", f"{variant}:{split}:{rotate}")
+    def _set(variant, division, rotate):
+        monkeypatch.setenv("DG_FORCE_CONFIG", f"{variant}:{division}:{rotate}")
     yield _set
     monkeypatch.delenv("DG_FORCE_CONFIG", raising=False)
+
+
+@pytest.fixture
+def num_cus():
+    dg = require_gpu()
+    yield dg.dg_set_num_cus
+    dg.dg_set_num_cus(0)
 
 
 def _workspace(dg, m, n, k, groups=1):
@@ -51,26 +63,47 @@ def dense_ops():
     return a, sfa, b, sfb, gemm.gemm_nt_ref(a, sfa, b, sfb)
 
 
+def _run_dense(dg, ops, what, ws=None):
+    a, sfa, b, sfb, ref = ops
+    d = torch.full((M, N), SENTINEL, dtype=torch.int16, device="cuda")
+    dg.dg_fp8_gemm_nt(dev(a), dev(sfa), dev(b), dev(sfb), d, workspace=ws if ws is not None else _workspace(dg, M, N, K))
+    check(bf16_to_f64(host(d)), ref, what)
+
+
 @pytest.mark.parametrize("rotate", [0, 1])
-@pytest.mark.parametrize("split", [1, 3])
+@pytest.mark.parametrize("division", [0, 1, 3])
 @pytest.mark.parametrize("variant", range(NUM_VARIANTS))
-def test_dense_every_variant(variant, split, rotate, force, dense_ops):
+def test_dense_every_variant(variant, division, rotate, force, dense_ops):
     dg = require_gpu()
-    force(variant, split, rotate)
+    force(variant, division, rotate)
     cfg = _config(dg, 0, M, N, K, 1)
     assert int(cfg["variant"]) == variant
+    assert int(cfg["stream_k"]) == (division > 0)
+    assert int(cfg["sk_split"]) == (division if division >= 2 else 0)
     assert int(cfg["k_rotate"]) == rotate
-    a, sfa, b, sfb, ref = dense_ops
-    d = torch.full((M, N), SENTINEL, dtype=torch.int16, device="cuda")
-    dg.dg_fp8_gemm_nt(dev(a), dev(sfa), dev(b), dev(sfb), d, workspace=_workspace(dg, M, N, K))
-    check(bf16_to_f64(host(d)), ref, f"variant {variant} split {cfg['split_k']} rotate {rotate}")
+    _run_dense(dg, dense_ops, f"variant {variant} division {division} rotate {rotate}")
 
 
-@pytest.mark.parametrize("split", [1, 3])
-@pytest.mark.parametrize("variant", range(NUM_VARIANTS))
-def test_masked_every_variant(variant, split, force):
+@pytest.mark.parametrize("cus", [1, 3, 13, 40, 200, 1000])
+@pytest.mark.parametrize("division", [1, 3])
+@pytest.mark.parametrize("variant", [0, 4, 6])
+def test_dense_stream_k_grids(variant, division, cus, force, num_cus, dense_ops):
     dg = require_gpu()
-    force(variant, split, 1)
+    force(variant, division, 1)
+    num_cus(cus)
+    cfg = _config(dg, 0, M, N, K, 1)
+    assert int(cfg["stream_k"]) == 1 and 1 <= int(cfg["grid"]) <= cus
+    ws = _workspace(dg, M, N, K)
+    _run_dense(dg, dense_ops, f"variant {variant} division {division} grid {cfg['grid']}", ws)
+    # A second call on the same workspace: every arrival counter was reset.
+    _run_dense(dg, dense_ops, f"variant {variant} division {division} grid {cfg['grid']}, second call", ws)
+
+
+@pytest.mark.parametrize("division", [0, 1, 3])
+@pytest.mark.parametrize("variant", range(NUM_VARIANTS))
+def test_masked_every_variant(variant, division, force):
+    dg = require_gpu()
+    force(variant, division, 1)
     g, m_max = 3, 160
     mm = np.array([150, 0, 77], dtype=np.int32)
     xa = bf16_normal((g, m_max, K), 511)
@@ -83,16 +116,17 @@ def test_masked_every_variant(variant, split, force):
     out = host(d)
     ref, written = gemm.grouped_masked_ref(a, sfa, b, sfb, mm)
     assert np.all(out[~written] == SENTINEL), f"variant {variant}: rows past masked_m written"
-    check(bf16_to_f64(out[written]), ref[written], f"masked variant {variant}")
+    check(bf16_to_f64(out[written]), ref[written], f"masked variant {variant} division {division}")
 
 
 @pytest.mark.parametrize("variant", range(NUM_VARIANTS))
 def test_contiguous_every_variant(variant, force):
     dg = require_gpu()
-    force(variant, 1, 1)
+    force(variant, 1, 1)  # stream-K is requested but the contiguous layout runs data-parallel
     g = 3
     mi = contiguous_m_indices([128, 384, 256], [0, 128, 0], [2, 0, 1])
     m_total = mi.size
+    assert int(_config(dg, 1, m_total, N, K, g)["stream_k"]) == 0
     xa = bf16_normal((m_total, K), 521)
     xb = bf16_normal((g, N, K), 522)
     a, sfa = quant.quant_1x128(xa)
