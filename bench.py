@@ -71,6 +71,13 @@ def parse_args(argv=None):
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work for the oracle sample")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain device copy of known size (for counter calibration)")
+    p.add_argument("--launches-only", metavar="WORKLOAD",
+                   help="only quantise and launch this workload's GEMM --reps times, no timing "
+                        "(the program rocprofv3 --pmc runs for the traffic counters)")
+    p.add_argument("--reps", type=int, default=5)
+    p.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                   help="write the traffic summary for --launches-only's workload from four rocprofv3 "
+                        "counter_collection.csv files (no GPU needed)")
     return p.parse_args(argv)
 
 
@@ -344,8 +351,98 @@ def _cpu_model():
 
 # -------------------------------------------------------------------- main --
 
+# ------------------------------------------------------------------ traffic --
+#
+# HBM traffic of the dominant kernel comes from two rocprofv3 --pmc runs of
+# `bench.py --launches-only W` (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch) and the same two counters read for a plain 256 MiB device copy
+# (`bench.py --calibrate-copy`), which scale them to bytes.  The summary is
+# kept under profiles/ with a hash of the kernel sources; the bench line
+# reports it only while the sources are unchanged.
+
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+KERNEL_SOURCES = ("dg_gemm.hip", "dg_device.h", "dg_internal.h")
+COPY_BYTES = 256 << 20
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "moe_grouped_gemm_02_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_per_dispatch(path, counter, name_part):
+    import csv
+    sums = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
+                sums[r["Dispatch_Id"]] = sums.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not sums:
+        raise SystemExit(f"no {counter} rows for kernels matching {name_part!r} in {path}")
+    return float(np.median(list(sums.values()))), len(sums)
+
+
+def write_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    fetch, nf = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", "gemm_kernel")
+    write, nw = _counter_per_dispatch(write_csv, "WRITE_SIZE", "gemm_kernel")
+    cfetch, _ = _counter_per_dispatch(copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
+    cwrite, _ = _counter_per_dispatch(copy_write_csv, "WRITE_SIZE", "copyBuffer")
+    fscale, wscale = COPY_BYTES / (cfetch * 1024), COPY_BYTES / (cwrite * 1024)
+    traffic = fetch * 1024 * fscale + write * 1024 * wscale
+    lines = [
+        f"workload={workload}",
+        f"kernel_source_sha256_16={kernel_source_hash()}",
+        f"fetch_kib_per_dispatch={fetch:.1f}  (median of {nf} dispatches)",
+        f"write_kib_per_dispatch={write:.1f}  (median of {nw} dispatches)",
+        f"copy_fetch_kib={cfetch:.1f}  copy_write_kib={cwrite:.1f}  (plain copy of {COPY_BYTES} bytes each way)",
+        f"fetch_scale={fscale:.4f}  write_scale={wscale:.4f}",
+        f"traffic_bytes_per_launch={traffic:.0f}",
+        "",
+        "commands (from the repository root, REPO = its absolute path):",
+        "  cd /tmp && export TMPDIR=/tmp",
+        "  rocprofv3 --pmc FETCH_SIZE -f csv -d $REPO/gpurun_out/pmc_copy_f -o p -- python3 $REPO/bench.py --calibrate-copy",
+        "  rocprofv3 --pmc WRITE_SIZE -f csv -d $REPO/gpurun_out/pmc_copy_w -o p -- python3 $REPO/bench.py --calibrate-copy",
+        f"  rocprofv3 --pmc FETCH_SIZE -f csv -d $REPO/gpurun_out/pmc_f -o p -- python3 $REPO/bench.py --launches-only {workload}",
+        f"  rocprofv3 --pmc WRITE_SIZE -f csv -d $REPO/gpurun_out/pmc_w -o p -- python3 $REPO/bench.py --launches-only {workload}",
+        f"  python3 bench.py --launches-only {workload} --write-traffic gpurun_out/pmc_f/p_counter_collection.csv "
+        "gpurun_out/pmc_w/p_counter_collection.csv gpurun_out/pmc_copy_f/p_counter_collection.csv "
+        "gpurun_out/pmc_copy_w/p_counter_collection.csv",
+    ]
+    path = os.path.join(PROFILES, f"gemm_kernel_{workload}_traffic.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+
+
+def read_traffic(workload):
+    """Bytes per launch from the committed summary, or None if there is none
+    for this workload or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"gemm_kernel_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith(" "):
+                k, v = line.split("=", 1)
+                fields[k.strip()] = v.split()[0]
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def main(argv=None):
     args = parse_args(argv)
+    if args.write_traffic:
+        if not args.launches_only:
+            raise SystemExit("--write-traffic needs --launches-only WORKLOAD")
+        write_traffic(args.launches_only, *args.write_traffic)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the library has no multi-GPU path).", file=sys.stderr)
@@ -363,6 +460,17 @@ def main(argv=None):
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_each_way": src.numel(), "launches": 5}))
+        return 0
+
+    if args.launches_only:
+        import synth
+        wl = {w.name: w for w in synth.workloads()}[args.launches_only]
+        p = Prepared(dg, torch, wl)
+        for r in range(args.reps):
+            p.quant(dg)
+            p.gemm(dg, r)
+        torch.cuda.synchronize()
+        print(json.dumps({"launches": args.reps, "workload": wl.name, "config": p.config}))
         return 0
 
     wls = select_workloads(args.workload)
@@ -401,13 +509,19 @@ def main(argv=None):
     mean_bytes = float(np.mean([preps[i].bytes for i in idx]))
     mean_dur = float(np.mean(gemm_ms[:, idx])) * 1e-3
     achieved = mean_bytes / mean_dur / 1e9
+    # Counter-measured HBM bytes per launch, when every shape of the kernel
+    # has a summary taken with the current kernel sources.
+    measured = [read_traffic(preps[i].wl.name) for i in idx]
+    traffic = float(np.mean(measured)) if measured and all(x is not None for x in measured) else None
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
-        "traffic": None,
+        "traffic": round(traffic) if traffic is not None else None,
+        "traffic_source": ([f"profiles/gemm_kernel_{preps[i].wl.name}_traffic.txt" for i in idx]
+                           if traffic is not None else None),
         "kernel": key,
         "launches_averaged": len(idx) * args.steps,
         "mean_algorithmic_bytes_per_launch": mean_bytes,
