@@ -184,6 +184,7 @@ int dg_quant_1x128(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
   if (cols % 128) return fail(DG_ERR_UNSUPPORTED_SHAPE, "cols=%d is not a multiple of 128", cols);
   if (ld_sf < rows) return fail(DG_ERR_INVALID_VALUE, "ld_sf smaller than rows");
   if (ld_sf % 4) return fail(DG_ERR_MISALIGNED, "ld_sf must be a multiple of 4");
+  if ((int64_t)num_groups * rows > INT32_MAX) return fail(DG_ERR_UNSUPPORTED_SHAPE, "num_groups * rows exceeds 2^31 - 1");
   if (!x || !q || !sf) return fail(DG_ERR_INVALID_VALUE, "null pointer argument");
   if (!aligned16(x) || !aligned16(q) || !aligned16(sf)) return fail(DG_ERR_MISALIGNED, "x, q and sf must be 16-byte aligned");
   if (cols == 0 || ld_sf == 0) return ok();

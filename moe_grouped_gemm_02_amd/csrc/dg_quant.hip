@@ -7,57 +7,81 @@
 // activation-scale layout: DeepGEMM project introduction, section Interfaces.
 //
 // Both kernels are HBM-bound streams (2 bytes read, ~1.03 bytes written per
-// element): loads are 16-byte vectors, one 128-element tile is owned by 16
-// consecutive lanes so a wave reads 1 KB of contiguous memory per step.
+// element) with 16-byte vector loads and stores.
 
 #include "dg_device.h"
 #include "dg_internal.h"
 
 namespace dg {
 
-// One 1x128 tile per 16 lanes; each lane owns 8 consecutive bf16 values.
+// Division and encoding, shared by both quantisers.
+//
+// q = fp32(x / s) is formed as fp32((double)x * RN64(1 / (double)s)): one
+// correctly rounded fp64 reciprocal per tile, then one fp64 multiply per
+// element.  For a bf16 x (8 significant bits) and an fp32 s (24 bits) the
+// exact quotient lies at least 2^-49 (relative) away from any fp32 rounding
+// boundary, while this product is within about 2^-52 of it, so rounding it
+// to fp32 gives the IEEE quotient itself (also checked exhaustively on the
+// host: every s = fp32(a / 448) over the positive finite bf16 a, against every
+// bf16 x with |x| <= a, 1.07e9 pairs, no difference).  A zero tile (s = 0)
+// uses a zero reciprocal, which keeps each x's signed zero.
+__device__ __forceinline__ double tile_reciprocal(float s) { return s == 0.0f ? 0.0 : 1.0 / (double)s; }
+
+__device__ __forceinline__ float quotient(uint32_t bf16_bits, double rcp) {
+  return (float)((double)bf16_bits_to_f32(bf16_bits) * rcp);
+}
+
+// e4m3 codes of four quotients, packed little-endian into one word, by the
+// hardware fp32 -> fp8 conversion (OCP e4m3fn, round to nearest even, signed
+// zero kept).  It agrees with the encoding rule of f32_to_e4m3_rne for every
+// fp32 value of magnitude below 450 (checked on gfx950 for all 2.28e9 such bit
+// patterns); quotients here are at most 448 * (1 + 2^-24).
+__device__ __forceinline__ uint32_t e4m3_x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// 1x128 activation tiles.  Block (x, y) covers tiles [32 x, 32 x + 32) of the
+// rows y, y + gridDim.y, ...; 8 consecutive lanes own one tile, 16 bf16
+// values (32 bytes) each, so a wave reads 2 KB of one row.
+constexpr int kQTilesPerBlock = 32;
+
 __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __restrict__ x,
                                                           uint8_t* __restrict__ q,
                                                           float* __restrict__ sf, int rows,
                                                           int cols, int64_t ld_sf, int groups) {
   const int tiles_per_row = cols / kBlockK;
-  const int64_t tiles = (int64_t)groups * rows * tiles_per_row;
-  const int sub = threadIdx.x & 15;  // lane within the tile's 16-lane group
-  const int64_t first = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
-  const int64_t step = ((int64_t)gridDim.x * blockDim.x) >> 4;
-  for (int64_t t = first; t < tiles; t += step) {
-    const int j = (int)(t % tiles_per_row);
-    const int64_t gr = t / tiles_per_row;  // g * rows + r
-    const int r = (int)(gr % rows);
-    const int g = (int)(gr / rows);
-    const int64_t elem = gr * cols + (int64_t)j * kBlockK + sub * 8;
-    const uint4 raw = *reinterpret_cast<const uint4*>(x + elem);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    float v[8];
-    float amax = 0.0f;
+  const int total_rows = groups * rows;
+  const int sub = threadIdx.x & 7;  // lane within the tile's 8-lane group
+  const int j = blockIdx.x * kQTilesPerBlock + (threadIdx.x >> 3);
+  if (j < tiles_per_row) {
+    for (int gr = blockIdx.y; gr < total_rows; gr += gridDim.y) {  // gr = g * rows + r
+      const int g = gr / rows, r = gr - g * rows;
+      const int64_t elem = (int64_t)gr * cols + j * kBlockK + sub * 16;
+      const uint4 lo = *reinterpret_cast<const uint4*>(x + elem);
+      const uint4 hi = *reinterpret_cast<const uint4*>(x + elem + 8);
+      const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
-      v[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
-      amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
+      for (int i = 0; i < 8; ++i)
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w[i] & 0xFFFFu)), fabsf(bf16_bits_to_f32(w[i] >> 16))));
+#pragma unroll
+      for (int off = 4; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 8));
+      const float s = amax / 448.0f;
+      const double rcp = tile_reciprocal(s);
+      uint32_t out[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        out[i] = e4m3_x4(quotient(w[2 * i] & 0xFFFFu, rcp), quotient(w[2 * i] >> 16, rcp),
+                         quotient(w[2 * i + 1] & 0xFFFFu, rcp), quotient(w[2 * i + 1] >> 16, rcp));
+      *reinterpret_cast<uint4*>(q + elem) = make_uint4(out[0], out[1], out[2], out[3]);
+      if (sub == 0) sf[((int64_t)g * tiles_per_row + j) * ld_sf + r] = s;
     }
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
-    const float s = amax / 448.0f;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t c = (s == 0.0f) ? ((__float_as_uint(v[i]) >> 24) & 0x80u)
-                                     : f32_to_e4m3_rne(v[i] / s);
-      if (i < 4) lo |= c << (8 * i);
-      else hi |= c << (8 * (i - 4));
-    }
-    *reinterpret_cast<uint2*>(q + elem) = make_uint2(lo, hi);
-    if (sub == 0) sf[((int64_t)g * tiles_per_row + j) * ld_sf + r] = s;
   }
   // Padding entries of the scale matrix (rows in [rows, ld_sf)) are zero.
   const int pad = (int)(ld_sf - rows);
-  if (pad > 0) {
+  if (pad > 0 && blockIdx.y == 0) {
     const int64_t pads = (int64_t)groups * tiles_per_row * pad;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pads;
          i += (int64_t)gridDim.x * blockDim.x) {
@@ -102,21 +126,17 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __re
   __syncthreads();
   amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
   const float s = amax / 448.0f;
+  const double rcp = tile_reciprocal(s);
   if (tid == 0) sf[((int64_t)g * nblocks + nb) * kblocks + kb] = s;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = nb * kBlockK + (tid >> 4) + 16 * i;
     if (r >= rows) continue;
     const uint32_t p[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t bits = (e & 1) ? (p[e >> 1] >> 16) : (p[e >> 1] & 0xFFFFu);
-      const float v = bf16_bits_to_f32(bits);
-      const uint32_t c = (s == 0.0f) ? ((bits >> 8) & 0x80u) : f32_to_e4m3_rne(v / s);
-      if (e < 4) lo |= c << (8 * e);
-      else hi |= c << (8 * (e - 4));
-    }
+    const uint32_t lo = e4m3_x4(quotient(p[0] & 0xFFFFu, rcp), quotient(p[0] >> 16, rcp),
+                                quotient(p[1] & 0xFFFFu, rcp), quotient(p[1] >> 16, rcp));
+    const uint32_t hi = e4m3_x4(quotient(p[2] & 0xFFFFu, rcp), quotient(p[2] >> 16, rcp),
+                                quotient(p[3] & 0xFFFFu, rcp), quotient(p[3] >> 16, rcp));
     *reinterpret_cast<uint2*>(q + base + (int64_t)r * cols + kb * kBlockK + chunk * 8) =
         make_uint2(lo, hi);
   }
@@ -124,14 +144,16 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __re
 
 hipError_t launch_quant_1x128(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
                               int64_t ld_sf, int groups, hipStream_t stream) {
-  const int64_t tiles = (int64_t)groups * rows * (cols / kBlockK);
-  const int64_t pads = (int64_t)groups * (cols / kBlockK) * (ld_sf - rows);
-  const int64_t want = (tiles * 16 > pads ? tiles * 16 : pads);
-  int64_t blocks = (want + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(quant_1x128_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, q, sf,
-                     rows, cols, ld_sf, groups);
+  const int tiles_per_row = cols / kBlockK;
+  const int gx = (tiles_per_row + kQTilesPerBlock - 1) / kQTilesPerBlock;
+  const int64_t total_rows = (int64_t)groups * rows;
+  // About 8 blocks per CU; every block walks its column of tiles down the rows.
+  int64_t gy = (2048 + gx - 1) / gx;
+  if (gy > total_rows) gy = total_rows;
+  if (gy > 65535) gy = 65535;
+  if (gy < 1) gy = 1;
+  hipLaunchKernelGGL(quant_1x128_kernel, dim3(gx > 0 ? gx : 1, (unsigned)gy), dim3(256), 0, stream, x, q,
+                     sf, rows, cols, ld_sf, groups);
   return hipGetLastError();
 }
 
