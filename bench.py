@@ -39,13 +39,29 @@ FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (no sparsity)
 MALL_BYTES = 256 << 20
 METRIC = "FP8 TFLOPS and HBM GB/s per shape, % of MI355X FP8/HBM roofline"
 
-# DeepGEMM performance tables (H800), TFLOPS per (layout, groups, m, n, k):
-# DeepGEMM project introduction, section Performance.  Used only as context.
-PAGES_TFLOPS = {
-    ("dense", 1, 128, 2112, 7168): 352, ("dense", 1, 128, 24576, 1536): 535,
-    ("dense", 1, 128, 32768, 512): 358, ("dense", 1, 128, 7168, 16384): 645,
-    ("dense", 1, 128, 4096, 7168): 533, ("dense", 1, 128, 7168, 2048): 510,
-}
+# DeepGEMM performance tables (H800), TFLOPS per (layout, groups, m per group,
+# n, k): DeepGEMM project introduction, section Performance, kept with their
+# citation in tests/golden/deepgemm_perf_tables.csv.  Context only.
+def _load_pages_tflops():
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tests", "golden", "deepgemm_perf_tables.csv")
+    table = {}
+    with open(path) as f:
+        rows = [line for line in f if line.strip() and not line.startswith("#")]
+    for line in rows[1:]:
+        layout, groups, m, n, k, tflops = line.split(",")[:6]
+        table[(layout, int(groups), int(m), int(n), int(k))] = float(tflops)
+    return table
+
+
+PAGES_TFLOPS = _load_pages_tflops()
+
+
+def pages_key(wl):
+    """The pages' table row of a workload, or None (random masked counts are not a row)."""
+    if wl.layout == "masked" and not wl.all_valid:
+        return None
+    key = (wl.layout, wl.groups, wl.m, wl.n, wl.k)
+    return key if key in PAGES_TFLOPS else None
 
 
 def algorithmic_flops(m_valid, n, k):
@@ -86,13 +102,17 @@ def parse_args(argv=None):
 def select_workloads(name):
     import synth
     wls = synth.workloads()
+    extra = synth.pages_workloads()
     if name == "decode128":
         return [w for w in wls if w.layout == "dense" and w.m == 128]
     if name == "all":
-        return wls
-    pick = [w for w in wls if w.name == name]
+        return wls + extra
+    if name == "pages":  # every row of the pages' performance tables
+        return [w for w in wls + extra if pages_key(w) is not None]
+    pick = [w for w in wls + extra if w.name == name]
     if not pick:
-        raise SystemExit(f"unknown workload {name}; choose from decode128, all, " + ", ".join(w.name for w in wls))
+        raise SystemExit(f"unknown workload {name}; choose from decode128, all, pages, "
+                         + ", ".join(w.name for w in wls + extra))
     return pick
 
 
@@ -133,7 +153,7 @@ class Prepared:
             self.mi = torch.from_numpy(synth.contiguous_m_indices([wl.m] * g)).to(dev)
             self.m_valid = g * wl.m
         elif wl.layout == "masked":
-            mm = synth.masked_m(g, wl.m)
+            mm = synth.workload_masked_m(wl)
             self.mm = torch.from_numpy(mm).to(dev)
             self.m_valid = int(mm.sum())
         else:
@@ -464,7 +484,7 @@ def main(argv=None):
 
     if args.launches_only:
         import synth
-        wl = {w.name: w for w in synth.workloads()}[args.launches_only]
+        wl = {w.name: w for w in synth.workloads() + synth.pages_workloads()}[args.launches_only]
         p = Prepared(dg, torch, wl)
         for r in range(args.reps):
             p.quant(dg)
@@ -489,7 +509,7 @@ def main(argv=None):
         per_shape.append(shape_record(p, t, time_quant(dg, torch, p)))
 
     extra = []
-    if args.workload == "all":
+    if args.workload in ("all", "pages"):
         for w in wls:
             if w in headline:
                 continue
@@ -528,10 +548,9 @@ def main(argv=None):
         "mean_launch_us": round(mean_dur * 1e6, 3),
     }
 
-    page_t = sum(2.0 * w.m * w.n * w.k / (PAGES_TFLOPS[("dense", 1, w.m, w.n, w.k)] * 1e12)
-                 for w in headline if ("dense", 1, w.m, w.n, w.k) in PAGES_TFLOPS)
     vs = None
-    if headline and all(("dense", 1, w.m, w.n, w.k) in PAGES_TFLOPS for w in headline):
+    if headline and all(pages_key(w) is not None for w in headline):
+        page_t = sum(p.flops / (PAGES_TFLOPS[pages_key(p.wl)] * 1e12) for p in preps)
         vs = round(value / (step_flops / page_t / 1e12), 4)
 
     result = {
@@ -568,7 +587,10 @@ def main(argv=None):
 def shape_record(p, t, quant_ms):
     tflops = p.flops / t / 1e12
     gbps = p.bytes / t / 1e9
+    key = pages_key(p.wl)
     return {
+        "pages_h800_tflops": PAGES_TFLOPS[key] if key else None,
+        "vs_pages": round(tflops / PAGES_TFLOPS[key], 3) if key else None,
         "workload": p.wl.name,
         "layout": p.wl.layout,
         "groups": p.wl.groups,

@@ -10,7 +10,8 @@ distribution, so i.i.d. N(0,1) values stand in for activations and weights):
   bf16 (torch's CPU cast), stored as uint16 bit patterns;
 * seeds: A = 1000 + workload number, B = 2000 + workload number;
 * contiguous m_indices: expert g repeated for its (128-aligned) segment;
-* masked_m: default_rng(3000).integers(1, M_max + 1, size=G).
+* masked_m: default_rng(3000).integers(1, M_max + 1, size=G), or M_max for
+  every group in the all-valid masked workloads of the pages' tables.
 """
 
 from dataclasses import dataclass, field
@@ -76,6 +77,17 @@ class Workload:
     def seed_b(self) -> int:
         return SEED_B + self.number
 
+    @property
+    def all_valid(self) -> bool:
+        return bool(self.extra.get("all_valid", False))
+
+
+def workload_masked_m(wl: "Workload") -> np.ndarray:
+    """masked_m of a masked workload: seeded random counts, or all rows valid."""
+    if wl.all_valid:
+        return np.full(wl.groups, wl.m, dtype=np.int32)
+    return masked_m(wl.groups, wl.m)
+
 
 NK_PAIRS = [(2112, 7168), (24576, 1536), (32768, 512), (7168, 16384), (4096, 7168), (7168, 2048)]
 
@@ -89,4 +101,23 @@ def workloads():
         out.append(Workload(f"dense_m4096_n{n}_k{k}", "dense", 4096, n, k, number=3))
     out.append(Workload("contiguous_g4_m8192_n4096_k7168", "contiguous", 8192, 4096, 7168, groups=4, number=4))
     out.append(Workload("masked_g4_mmax1024_n4096_k7168", "masked", 1024, 4096, 7168, groups=4, number=5))
+    return out
+
+
+def pages_workloads():
+    """The rows of the pages' performance tables (DeepGEMM project introduction,
+    section Performance) not already among workloads(): dense M = 64 at the
+    other five (N, K) pairs, contiguous 4 x 8192 at (7168, 2048) and 8 x 4096 at
+    both pairs, masked 1 x 1024, 2 x 512 and 4 x 256 with every row valid at
+    both pairs.  Seeds follow the workload numbers of workloads()."""
+    out = []
+    for n, k in NK_PAIRS[1:]:
+        out.append(Workload(f"dense_m64_n{n}_k{k}", "dense", 64, n, k, number=1))
+    out.append(Workload("contiguous_g4_m8192_n7168_k2048", "contiguous", 8192, 7168, 2048, groups=4, number=4))
+    for n, k in [(4096, 7168), (7168, 2048)]:
+        out.append(Workload(f"contiguous_g8_m4096_n{n}_k{k}", "contiguous", 4096, n, k, groups=8, number=4))
+    for g, mm in [(1, 1024), (2, 512), (4, 256)]:
+        for n, k in [(4096, 7168), (7168, 2048)]:
+            out.append(Workload(f"masked_g{g}_m{mm}_full_n{n}_k{k}", "masked", mm, n, k, groups=g, number=5,
+                                extra={"all_valid": True}))
     return out

@@ -21,7 +21,8 @@ from tests.tolerance import check
 
 pytestmark = pytest.mark.gpu
 
-WORKLOADS = synth.workloads()
+# The five benchmark workloads and the remaining rows of the pages' tables.
+WORKLOADS = synth.workloads() + synth.pages_workloads()
 
 
 def _sample_rows(rows, count, rng):
@@ -89,10 +90,10 @@ def test_dense_workload_sampled(wl):
     assert not np.any(host(d) == SENTINEL)
 
 
-def test_contiguous_workload_sampled():
+@pytest.mark.parametrize("wl", [w for w in WORKLOADS if w.layout == "contiguous"], ids=lambda w: w.name)
+def test_contiguous_workload_sampled(wl):
     dg = require_gpu()
-    wl = next(w for w in WORKLOADS if w.layout == "contiguous")
-    rng = np.random.default_rng(44)
+    rng = np.random.default_rng(44 + wl.n + wl.groups)
     g, mg, n, k = wl.groups, wl.m, wl.n, wl.k
     m_total = g * mg
     mi = synth.contiguous_m_indices([mg] * g)
@@ -127,12 +128,12 @@ def test_contiguous_workload_sampled():
         check(bf16_to_f64(d_h[np.ix_(rg, cols)]), ref, f"{wl.name} group {grp}")
 
 
-def test_masked_workload_sampled():
+@pytest.mark.parametrize("wl", [w for w in WORKLOADS if w.layout == "masked"], ids=lambda w: w.name)
+def test_masked_workload_sampled(wl):
     dg = require_gpu()
-    wl = next(w for w in WORKLOADS if w.layout == "masked")
-    rng = np.random.default_rng(55)
+    rng = np.random.default_rng(55 + wl.n + wl.groups)
     g, m_max, n, k = wl.groups, wl.m, wl.n, wl.k
-    mm = synth.masked_m(g, m_max)
+    mm = synth.workload_masked_m(wl)
     xa = synth.bf16_normal((g, m_max, k), wl.seed_a)
     xb = synth.bf16_normal((g, n, k), wl.seed_b)
     a = torch.empty((g, m_max, k), dtype=torch.uint8, device="cuda")
