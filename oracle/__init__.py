@@ -10,6 +10,8 @@ Contents
 --------
 e4m3      OCP e4m3fn decode table and round-to-nearest-even encoder.
 quant     1x128 activation and 128x128 weight quantisers (amax/448 scales).
+ue8m0     the same quantisers with power-of-two (UE8M0) scales: the smallest
+          power of two not below amax/448.
 gemm      dense NT, grouped-contiguous and grouped-masked reference GEMMs that
           accumulate each 128-wide K slice exactly in fp64, scale it by
           sa*sb and promote it; plus an exact-rational brute force.
@@ -23,7 +25,7 @@ Sources (the method is described on public pages about DeepSeek's DeepGEMM):
   "Technical background and core principles": 1x128 activation tiles,
   128x128 weight blocks, promotion every N_C = 128 elements of K.
 * "DeepGEMM: efficient BLAS kernel library on GPU" (yfxerp.com), section 3.1:
-  scale factors are FP32 on SM90.
+  scale factors are FP32 on SM90, packed UE8M0 on SM100.
 
 Readings where the pages are silent (e4m3 flavour, the amax/448 scale
 formula, the x/s quotient, all-zero tiles, saturation, the -1 convention for
@@ -35,4 +37,4 @@ tests/test_oracle_*.py against things other than itself (torch's CPU e4m3
 cast, exact rational brute force, closed forms, invariants).
 """
 
-from . import bf16, e4m3, gemm, quant  # noqa: F401
+from . import bf16, e4m3, gemm, quant, ue8m0  # noqa: F401
