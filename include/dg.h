@@ -115,6 +115,39 @@ int dg_grouped_masked(const uint8_t* a, const float* sfa, const uint8_t* b, cons
                       int k, int expected_m, int64_t ld_sfa, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/*
+ * The three GEMMs with power-of-two (UE8M0) scales.  The yfxerp.com DeepGEMM
+ * article (section 3.1) gives the scale factors of the newer architecture as
+ * UE8M0 - an unsigned 8-bit exponent E standing for 2^(E-127) - packed four
+ * to a 32-bit word, in place of fp32.  The product is the same formula as
+ * above with sfa and sfb replaced by 2^(E-127); since the scales are powers of
+ * two the kernel applies them inside the block-scaled matrix instruction
+ * instead of on the accumulator.  Scale layouts (bytes, MN-major for both
+ * operands, four consecutive rows or column blocks per dword):
+ *   sfa [k/128][ld_sfa] uint8 (masked: [num_groups][k/128][ld_sfa]);
+ *       ld_sfa >= rows, a multiple of 4 (dg_get_sf_leading_dim)
+ *   sfb [num_groups][k/128][ld_sfb] uint8 with
+ *       ld_sfb = dg_get_ue8m0_sfb_leading_dim(n) = round_up(ceil(n/128), 4)
+ * Everything else (operands, output, workspace, rules, errors) is as for the
+ * fp32-scale entry point of the same layout.  Exponent 255 (NaN in E8M0) is
+ * outside the contract; the quantisers below never write it.  A tile shape
+ * that has no UE8M0 instance (only possible through a forced configuration)
+ * returns DG_ERR_UNSUPPORTED_SHAPE.
+ */
+int dg_fp8_gemm_nt_ue8m0(const uint8_t* a, const uint8_t* sfa, const uint8_t* b,
+                         const uint8_t* sfb, uint16_t* d, int m, int n, int k, int64_t lda,
+                         int64_t ldb, int64_t ldd, int64_t ld_sfa, void* workspace,
+                         size_t workspace_bytes, void* stream);
+int dg_grouped_contiguous_ue8m0(const uint8_t* a, const uint8_t* sfa, const uint8_t* b,
+                                const uint8_t* sfb, uint16_t* d, const int32_t* m_indices,
+                                int m_total, int n, int k, int num_groups, int64_t ld_sfa,
+                                void* workspace, size_t workspace_bytes, void* stream);
+int dg_grouped_masked_ue8m0(const uint8_t* a, const uint8_t* sfa, const uint8_t* b,
+                            const uint8_t* sfb, uint16_t* d, const int32_t* masked_m,
+                            int num_groups, int m_max, int n, int k, int expected_m,
+                            int64_t ld_sfa, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* ----------------------------------------------------------- quantisers -- */
 
 /*
@@ -146,6 +179,25 @@ int dg_quant_1x128(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
 int dg_quant_128x128(const uint16_t* w, uint8_t* q, float* sf, int rows, int cols,
                      int num_groups, void* stream);
 
+/*
+ * The two quantisers with UE8M0 scales (scale format: yfxerp.com DeepGEMM
+ * article, section 3.1; the pages do not say how the exponent is chosen).
+ * Each tile or block takes the smallest power of two not below amax/448:
+ *   E = ceil(log2(amax / 448)) + 127 on the exact quotient, clamped to
+ *   [0, 254]; an all-zero tile gets E = 0;  s = 2^(E-127);
+ *   q = e4m3( fp32(x / s) ) with the same rounding and clamping as above
+ *   (x / s only shifts the exponent, so it is exact for normal results).
+ * dg_quant_1x128_ue8m0: x, q as dg_quant_1x128;
+ *   sf [num_groups][cols/128][ld_sf] uint8, rows [rows, ld_sf) written as 0.
+ * dg_quant_128x128_ue8m0: w, q as dg_quant_128x128;
+ *   sf [num_groups][cols/128][ld_sfb] uint8 (MN-major, unlike the fp32 weight
+ *   scales), ld_sfb = dg_get_ue8m0_sfb_leading_dim(rows), pads written as 0.
+ */
+int dg_quant_1x128_ue8m0(const uint16_t* x, uint8_t* q, uint8_t* sf, int rows, int cols,
+                         int64_t ld_sf, int num_groups, void* stream);
+int dg_quant_128x128_ue8m0(const uint16_t* w, uint8_t* q, uint8_t* sf, int rows, int cols,
+                           int num_groups, void* stream);
+
 /* -------------------------------------------------------------- utilities -- */
 
 /* Workspace bytes a GEMM of this shape needs (0 when it needs none).  For the
@@ -172,6 +224,10 @@ int dg_get_m_alignment_for_contiguous_layout(void);
  * (get_tma_aligned_size; section Utility functions): round_up(m, 4), so that
  * every column starts 16-byte aligned.  Returns -1 for m < 0. */
 int64_t dg_get_sf_leading_dim(int m);
+
+/* Leading dimension of the UE8M0 weight-scale matrix for n rows of B:
+ * round_up(ceil(n/128), 4) bytes.  Returns -1 for n < 0. */
+int64_t dg_get_ue8m0_sfb_leading_dim(int n);
 
 /* Text of the last error on the calling thread ("" if none). */
 const char* dg_get_last_error_string(void);

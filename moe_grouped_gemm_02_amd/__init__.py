@@ -9,6 +9,7 @@ the library has not been built (see build.py).
 Tensor conventions (torch dtypes standing in for the C types):
   e4m3 codes     torch.uint8       bf16 values  torch.bfloat16 (or int16 bits)
   fp32 scales    torch.float32     ids/counts   torch.int32
+  UE8M0 scales   torch.uint8 (exponent bytes, 2^(E-127))
 """
 
 import ctypes
@@ -33,8 +34,14 @@ _SIGNATURES = {
     "dg_fp8_gemm_nt": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _L, _L, _P, _S, _P]),
     "dg_grouped_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _P, _S, _P]),
     "dg_grouped_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _P, _S, _P]),
+    "dg_fp8_gemm_nt_ue8m0": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _L, _L, _P, _S, _P]),
+    "dg_grouped_contiguous_ue8m0": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _P, _S, _P]),
+    "dg_grouped_masked_ue8m0": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _P, _S, _P]),
     "dg_quant_1x128": (_I, [_P, _P, _P, _I, _I, _L, _I, _P]),
     "dg_quant_128x128": (_I, [_P, _P, _P, _I, _I, _I, _P]),
+    "dg_quant_1x128_ue8m0": (_I, [_P, _P, _P, _I, _I, _L, _I, _P]),
+    "dg_quant_128x128_ue8m0": (_I, [_P, _P, _P, _I, _I, _I, _P]),
+    "dg_get_ue8m0_sfb_leading_dim": (_L, [_I]),
     "dg_get_workspace_size": (_S, [_I, _I, _I, _I]),
     "dg_get_num_cus": (_I, []),
     "dg_set_num_cus": (_I, [_I]),
@@ -101,52 +108,71 @@ def _contig(t, name):
 
 
 # ------------------------------------------------------------------ GEMMs --
+#
+# Each GEMM and quantiser has an fp32-scale form and a UE8M0 form (power-of-two
+# scales stored as exponent bytes).  Scale shapes:
+#   fp32:  sfa [(G)][K/128][ld] float32,  sfb [(G)][ceil(N/128)][K/128] float32
+#   UE8M0: sfa [(G)][K/128][ld] uint8,    sfb [(G)][K/128][ld_sfb] uint8,
+#          ld_sfb = dg_get_ue8m0_sfb_leading_dim(N)
 
-def dg_fp8_gemm_nt(a, sfa, b, sfb, d, workspace=None):
-    """d[m][n] = bf16(A . B^T) with 1x128 (sfa [K/128][ld]) and 128x128 scales."""
+
+def _ue8m0_sfb_ld(n):
+    return ((n + 127) // 128 + 3) // 4 * 4
+
+
+def _sf_dtype(ue8m0):
+    return (torch.uint8,) if ue8m0 else (torch.float32,)
+
+
+def _sfb_shape(n, k, ue8m0):
+    return (k // 128, _ue8m0_sfb_ld(n)) if ue8m0 else ((n + 127) // 128, k // 128)
+
+
+def _ws(workspace):
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
+def _gemm_nt(fn, a, sfa, b, sfb, d, workspace, ue8m0):
     _expect(a, "a", _U8, 2), _expect(b, "b", _U8, 2), _expect(d, "d", _BF, 2)
-    _expect(sfa, "sfa", (torch.float32,), 2), _expect(sfb, "sfb", (torch.float32,), 2)
+    _expect(sfa, "sfa", _sf_dtype(ue8m0), 2), _expect(sfb, "sfb", _sf_dtype(ue8m0), 2)
     m, k = a.shape
     n = b.shape[0]
     if b.shape[1] != k or tuple(d.shape) != (m, n):
         raise ValueError("shape mismatch between a, b and d")
-    if sfa.shape[0] != k // 128 or tuple(sfb.shape) != ((n + 127) // 128, k // 128):
-        raise ValueError("scale shapes must be sfa [K/128][ld] and sfb [ceil(N/128)][K/128]")
+    if sfa.shape[0] != k // 128 or tuple(sfb.shape) != _sfb_shape(n, k, ue8m0):
+        raise ValueError(f"scale shapes must be sfa [K/128][ld] and sfb {_sfb_shape(n, k, ue8m0)}")
     for t, nm in ((a, "a"), (b, "b"), (d, "d"), (sfa, "sfa")):
         _row_major(t, nm)
     _contig(sfb, "sfb")
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("dg_fp8_gemm_nt", _lib.dg_fp8_gemm_nt(
+    _check(fn, getattr(_lib, fn)(
         _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), m, n, k, a.stride(0), b.stride(0),
-        d.stride(0), sfa.stride(0), _ptr(workspace), ws_bytes, _stream(d)))
+        d.stride(0), sfa.stride(0), _ptr(workspace), _ws(workspace), _stream(d)))
     return d
 
 
-def dg_grouped_contiguous(a, sfa, b, sfb, d, m_indices, workspace=None):
-    """Contiguous grouped GEMM; b [G][N][K], m_indices [M_total] int32."""
+def _contiguous(fn, a, sfa, b, sfb, d, m_indices, workspace, ue8m0):
     _expect(a, "a", _U8, 2), _expect(b, "b", _U8, 3), _expect(d, "d", _BF, 2)
-    _expect(sfa, "sfa", (torch.float32,), 2), _expect(sfb, "sfb", (torch.float32,), 3)
+    _expect(sfa, "sfa", _sf_dtype(ue8m0), 2), _expect(sfb, "sfb", _sf_dtype(ue8m0), 3)
     _expect(m_indices, "m_indices", (torch.int32,), 1)
     m_total, k = a.shape
     groups, n = b.shape[0], b.shape[1]
     if b.shape[2] != k or tuple(d.shape) != (m_total, n) or m_indices.shape[0] != m_total:
         raise ValueError("shape mismatch between a, b, d and m_indices")
-    if sfa.shape[0] != k // 128 or tuple(sfb.shape) != (groups, (n + 127) // 128, k // 128):
-        raise ValueError("scale shapes must be sfa [K/128][ld] and sfb [G][ceil(N/128)][K/128]")
+    want_b = (groups,) + _sfb_shape(n, k, ue8m0)
+    if sfa.shape[0] != k // 128 or tuple(sfb.shape) != want_b:
+        raise ValueError(f"scale shapes must be sfa [K/128][ld] and sfb {want_b}")
     for t, nm in ((a, "a"), (b, "b"), (d, "d"), (sfb, "sfb"), (m_indices, "m_indices")):
         _contig(t, nm)
     _row_major(sfa, "sfa")
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("dg_grouped_contiguous", _lib.dg_grouped_contiguous(
+    _check(fn, getattr(_lib, fn)(
         _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), _ptr(m_indices), m_total, n, k,
-        groups, sfa.stride(0), _ptr(workspace), ws_bytes, _stream(d)))
+        groups, sfa.stride(0), _ptr(workspace), _ws(workspace), _stream(d)))
     return d
 
 
-def dg_grouped_masked(a, sfa, b, sfb, d, masked_m, expected_m=0, workspace=None):
-    """Masked grouped GEMM; a [G][M_max][K], sfa [G][K/128][ld], masked_m [G] int32."""
+def _masked(fn, a, sfa, b, sfb, d, masked_m, expected_m, workspace, ue8m0):
     _expect(a, "a", _U8, 3), _expect(b, "b", _U8, 3), _expect(d, "d", _BF, 3)
-    _expect(sfa, "sfa", (torch.float32,), 3), _expect(sfb, "sfb", (torch.float32,), 3)
+    _expect(sfa, "sfa", _sf_dtype(ue8m0), 3), _expect(sfb, "sfb", _sf_dtype(ue8m0), 3)
     _expect(masked_m, "masked_m", (torch.int32,), 1)
     groups, m_max, k = a.shape
     n = b.shape[1]
@@ -154,22 +180,51 @@ def dg_grouped_masked(a, sfa, b, sfb, d, masked_m, expected_m=0, workspace=None)
         raise ValueError("shape mismatch between a, b and d")
     if masked_m.shape[0] != groups:
         raise ValueError("masked_m must have one entry per group")
-    if sfa.shape[:2] != (groups, k // 128) or tuple(sfb.shape) != (groups, (n + 127) // 128, k // 128):
-        raise ValueError("scale shapes must be sfa [G][K/128][ld] and sfb [G][ceil(N/128)][K/128]")
+    want_b = (groups,) + _sfb_shape(n, k, ue8m0)
+    if sfa.shape[:2] != (groups, k // 128) or tuple(sfb.shape) != want_b:
+        raise ValueError(f"scale shapes must be sfa [G][K/128][ld] and sfb {want_b}")
     for t, nm in ((a, "a"), (b, "b"), (d, "d"), (sfa, "sfa"), (sfb, "sfb"), (masked_m, "masked_m")):
         _contig(t, nm)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("dg_grouped_masked", _lib.dg_grouped_masked(
+    _check(fn, getattr(_lib, fn)(
         _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), _ptr(masked_m), groups, m_max, n, k,
-        int(expected_m), sfa.shape[2], _ptr(workspace), ws_bytes, _stream(d)))
+        int(expected_m), sfa.shape[2], _ptr(workspace), _ws(workspace), _stream(d)))
     return d
+
+
+def dg_fp8_gemm_nt(a, sfa, b, sfb, d, workspace=None):
+    """d[m][n] = bf16(A . B^T) with 1x128 (sfa [K/128][ld]) and 128x128 scales."""
+    return _gemm_nt("dg_fp8_gemm_nt", a, sfa, b, sfb, d, workspace, False)
+
+
+def dg_fp8_gemm_nt_ue8m0(a, sfa, b, sfb, d, workspace=None):
+    """dg_fp8_gemm_nt with exponent-byte scales (sfb [K/128][ld_sfb] uint8)."""
+    return _gemm_nt("dg_fp8_gemm_nt_ue8m0", a, sfa, b, sfb, d, workspace, True)
+
+
+def dg_grouped_contiguous(a, sfa, b, sfb, d, m_indices, workspace=None):
+    """Contiguous grouped GEMM; b [G][N][K], m_indices [M_total] int32."""
+    return _contiguous("dg_grouped_contiguous", a, sfa, b, sfb, d, m_indices, workspace, False)
+
+
+def dg_grouped_contiguous_ue8m0(a, sfa, b, sfb, d, m_indices, workspace=None):
+    """dg_grouped_contiguous with exponent-byte scales (sfb [G][K/128][ld_sfb])."""
+    return _contiguous("dg_grouped_contiguous_ue8m0", a, sfa, b, sfb, d, m_indices, workspace, True)
+
+
+def dg_grouped_masked(a, sfa, b, sfb, d, masked_m, expected_m=0, workspace=None):
+    """Masked grouped GEMM; a [G][M_max][K], sfa [G][K/128][ld], masked_m [G] int32."""
+    return _masked("dg_grouped_masked", a, sfa, b, sfb, d, masked_m, expected_m, workspace, False)
+
+
+def dg_grouped_masked_ue8m0(a, sfa, b, sfb, d, masked_m, expected_m=0, workspace=None):
+    """dg_grouped_masked with exponent-byte scales (sfb [G][K/128][ld_sfb])."""
+    return _masked("dg_grouped_masked_ue8m0", a, sfa, b, sfb, d, masked_m, expected_m, workspace, True)
 
 
 # ------------------------------------------------------------- quantisers --
 
-def dg_quant_1x128(x, q, sf):
-    """x [R][C] or [G][R][C] bf16 -> q e4m3 codes, sf [(G)][C/128][ld] fp32."""
-    _expect(x, "x", _BF), _expect(q, "q", _U8), _expect(sf, "sf", (torch.float32,))
+def _quant_1x128(fn, x, q, sf, ue8m0):
+    _expect(x, "x", _BF), _expect(q, "q", _U8), _expect(sf, "sf", _sf_dtype(ue8m0))
     if x.dim() not in (2, 3) or q.shape != x.shape or sf.dim() != x.dim():
         raise ValueError("x, q must match and sf must have the same rank")
     groups = 1 if x.dim() == 2 else x.shape[0]
@@ -178,26 +233,47 @@ def dg_quant_1x128(x, q, sf):
         raise ValueError("sf must be [(G)][C/128][ld]")
     for t, nm in ((x, "x"), (q, "q"), (sf, "sf")):
         _contig(t, nm)
-    _check("dg_quant_1x128", _lib.dg_quant_1x128(
+    _check(fn, getattr(_lib, fn)(
         _ptr(x), _ptr(q), _ptr(sf), rows, cols, sf.shape[-1], groups, _stream(x)))
     return q, sf
 
 
-def dg_quant_128x128(w, q, sf):
-    """w [N][K] or [G][N][K] bf16 -> q e4m3 codes, sf [(G)][ceil(N/128)][K/128] fp32."""
-    _expect(w, "w", _BF), _expect(q, "q", _U8), _expect(sf, "sf", (torch.float32,))
+def _quant_128x128(fn, w, q, sf, ue8m0):
+    _expect(w, "w", _BF), _expect(q, "q", _U8), _expect(sf, "sf", _sf_dtype(ue8m0))
     if w.dim() not in (2, 3) or q.shape != w.shape:
         raise ValueError("w and q must match")
     groups = 1 if w.dim() == 2 else w.shape[0]
     rows, cols = w.shape[-2], w.shape[-1]
-    want = ((rows + 127) // 128, cols // 128) if w.dim() == 2 else (groups, (rows + 127) // 128, cols // 128)
+    want = _sfb_shape(rows, cols, ue8m0)
+    if w.dim() == 3:
+        want = (groups,) + want
     if tuple(sf.shape) != want:
         raise ValueError(f"sf must have shape {want}")
     for t, nm in ((w, "w"), (q, "q"), (sf, "sf")):
         _contig(t, nm)
-    _check("dg_quant_128x128", _lib.dg_quant_128x128(
+    _check(fn, getattr(_lib, fn)(
         _ptr(w), _ptr(q), _ptr(sf), rows, cols, groups, _stream(w)))
     return q, sf
+
+
+def dg_quant_1x128(x, q, sf):
+    """x [R][C] or [G][R][C] bf16 -> q e4m3 codes, sf [(G)][C/128][ld] fp32."""
+    return _quant_1x128("dg_quant_1x128", x, q, sf, False)
+
+
+def dg_quant_1x128_ue8m0(x, q, sf):
+    """x [R][C] or [G][R][C] bf16 -> q e4m3 codes, sf [(G)][C/128][ld] uint8 exponents."""
+    return _quant_1x128("dg_quant_1x128_ue8m0", x, q, sf, True)
+
+
+def dg_quant_128x128(w, q, sf):
+    """w [N][K] or [G][N][K] bf16 -> q e4m3 codes, sf [(G)][ceil(N/128)][K/128] fp32."""
+    return _quant_128x128("dg_quant_128x128", w, q, sf, False)
+
+
+def dg_quant_128x128_ue8m0(w, q, sf):
+    """w [N][K] or [G][N][K] bf16 -> q e4m3 codes, sf [(G)][K/128][ld_sfb] uint8 exponents."""
+    return _quant_128x128("dg_quant_128x128_ue8m0", w, q, sf, True)
 
 
 # -------------------------------------------------------------- utilities --
@@ -223,6 +299,10 @@ def dg_get_m_alignment_for_contiguous_layout():
 
 def dg_get_sf_leading_dim(m):
     return int(_lib.dg_get_sf_leading_dim(int(m)))
+
+
+def dg_get_ue8m0_sfb_leading_dim(n):
+    return int(_lib.dg_get_ue8m0_sfb_leading_dim(int(n)))
 
 
 def dg_get_last_error_string():

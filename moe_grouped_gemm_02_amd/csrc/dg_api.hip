@@ -66,7 +66,7 @@ const char* layout_name(int layout) {
 
 // Shared checks for the three GEMM entry points.  rows = the rows of the
 // layout's row space (M, M_total or M_max).
-int check_gemm_common(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+int check_gemm_common(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb,
                       const uint16_t* d, int rows, int n, int k, int64_t lda, int64_t ldb,
                       int64_t ldd, int64_t ld_sfa) {
   if (rows < 0 || n < 0 || k < 0) return fail(DG_ERR_INVALID_VALUE, "negative dimension (m=%d n=%d k=%d)", rows, n, k);
@@ -104,6 +104,8 @@ int run_gemm(int layout, dg::GemmParams& p, int rows, int groups, void* ws, size
   const int cus = resolve_num_cus();
   if (cus < 0) return fail(DG_ERR_HIP, "cannot query the device's compute-unit count");
   const dg::GemmConfig cfg = dg::choose_config(layout, rows, p.n, p.k, groups, cus, expected_m);
+  if (p.sf_ue8m0 && !dg::ue8m0_variant_built(cfg.variant))
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "tile variant %d is not built for UE8M0 scales", cfg.variant);
   int st = check_workspace(cfg, layout, rows, p.n, groups, ws, ws_bytes);
   if (st != DG_SUCCESS) return st;
   p.workspace = static_cast<float*>(ws);
@@ -117,27 +119,33 @@ int run_gemm(int layout, dg::GemmParams& p, int rows, int groups, void* ws, size
   return ok();
 }
 
-}  // namespace
+// Scale-format fields of GemmParams.  fp32: weight scales [G][ceil(N/128)][K/128].
+// UE8M0: exponent bytes, weights MN-major [G][K/128][ld_sfb].
+void set_scales(dg::GemmParams& p, const void* sfa, const void* sfb, int n, int k, bool ue8m0) {
+  p.sfa = static_cast<const float*>(sfa);
+  p.sfb = static_cast<const float*>(sfb);
+  p.sf_ue8m0 = ue8m0 ? 1 : 0;
+  p.ld_sfb = ue8m0 ? (((int64_t)(n + 127) / 128 + 3) / 4 * 4) : 0;
+  p.sfb_gstride = ue8m0 ? (int64_t)(k / 128) * p.ld_sfb : (int64_t)((n + 127) / 128) * (k / 128);
+}
 
-extern "C" {
-
-int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
-                   uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
-                   int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream) {
+int gemm_nt_impl(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb, uint16_t* d,
+                 int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd, int64_t ld_sfa,
+                 void* workspace, size_t workspace_bytes, void* stream, bool ue8m0) {
   int st = check_gemm_common(a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa);
   if (st != DG_SUCCESS) return st;
   if (m == 0 || n == 0) return ok();
   dg::GemmParams p{};
-  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d;
+  p.a = a; p.b = b; p.d = d;
+  set_scales(p, sfa, sfb, n, k, ue8m0);
   p.m = m; p.n = n; p.k = k; p.num_groups = 1;
   p.lda = lda; p.ldb = ldb; p.ldd = ldd; p.ld_sfa = ld_sfa;
   return run_gemm(dg::kDense, p, m, 1, workspace, workspace_bytes, stream);
 }
 
-int dg_grouped_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
-                          const float* sfb, uint16_t* d, const int32_t* m_indices,
-                          int m_total, int n, int k, int num_groups, int64_t ld_sfa,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+int contiguous_impl(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb, uint16_t* d,
+                    const int32_t* m_indices, int m_total, int n, int k, int num_groups, int64_t ld_sfa,
+                    void* workspace, size_t workspace_bytes, void* stream, bool ue8m0) {
   if (num_groups < 1) return fail(DG_ERR_INVALID_VALUE, "num_groups must be >= 1");
   int st = check_gemm_common(a, sfa, b, sfb, d, m_total, n, k, k, k, n, ld_sfa);
   if (st != DG_SUCCESS) return st;
@@ -146,18 +154,17 @@ int dg_grouped_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
   if (n % 8) return fail(DG_ERR_MISALIGNED, "n must be a multiple of 8 (rows of d are packed)");
   if (m_total == 0 || n == 0) return ok();
   dg::GemmParams p{};
-  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.m_indices = m_indices;
+  p.a = a; p.b = b; p.d = d; p.m_indices = m_indices;
+  set_scales(p, sfa, sfb, n, k, ue8m0);
   p.m = m_total; p.n = n; p.k = k; p.num_groups = num_groups;
   p.lda = k; p.ldb = k; p.ldd = n; p.ld_sfa = ld_sfa;
   p.b_gstride = (int64_t)n * k;
-  p.sfb_gstride = (int64_t)((n + 127) / 128) * (k / 128);
   return run_gemm(dg::kContiguous, p, m_total, num_groups, workspace, workspace_bytes, stream);
 }
 
-int dg_grouped_masked(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
-                      uint16_t* d, const int32_t* masked_m, int num_groups, int m_max, int n,
-                      int k, int expected_m, int64_t ld_sfa, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+int masked_impl(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb, uint16_t* d,
+                const int32_t* masked_m, int num_groups, int m_max, int n, int k, int expected_m,
+                int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream, bool ue8m0) {
   if (num_groups < 1) return fail(DG_ERR_INVALID_VALUE, "num_groups must be >= 1");
   if (expected_m < 0) return fail(DG_ERR_INVALID_VALUE, "expected_m must be >= 0");
   int st = check_gemm_common(a, sfa, b, sfb, d, m_max, n, k, k, k, n, ld_sfa);
@@ -167,19 +174,19 @@ int dg_grouped_masked(const uint8_t* a, const float* sfa, const uint8_t* b, cons
   if (num_groups > 65535) return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many groups");
   if (m_max == 0 || n == 0) return ok();
   dg::GemmParams p{};
-  p.a = a; p.sfa = sfa; p.b = b; p.sfb = sfb; p.d = d; p.masked_m = masked_m;
+  p.a = a; p.b = b; p.d = d; p.masked_m = masked_m;
+  set_scales(p, sfa, sfb, n, k, ue8m0);
   p.m = m_max; p.n = n; p.k = k; p.num_groups = num_groups;
   p.lda = k; p.ldb = k; p.ldd = n; p.ld_sfa = ld_sfa;
   p.a_gstride = (int64_t)m_max * k;
   p.sfa_gstride = (int64_t)(k / 128) * ld_sfa;
   p.b_gstride = (int64_t)n * k;
-  p.sfb_gstride = (int64_t)((n + 127) / 128) * (k / 128);
   p.d_gstride = (int64_t)m_max * n;
   return run_gemm(dg::kMasked, p, m_max, num_groups, workspace, workspace_bytes, stream, expected_m);
 }
 
-int dg_quant_1x128(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
-                   int64_t ld_sf, int num_groups, void* stream) {
+int quant_1x128_impl(const uint16_t* x, uint8_t* q, void* sf, int rows, int cols, int64_t ld_sf,
+                     int num_groups, bool pow2, void* stream) {
   if (rows < 0 || cols < 0 || num_groups < 1) return fail(DG_ERR_INVALID_VALUE, "bad sizes (rows=%d cols=%d groups=%d)", rows, cols, num_groups);
   if (cols % 128) return fail(DG_ERR_UNSUPPORTED_SHAPE, "cols=%d is not a multiple of 128", cols);
   if (ld_sf < rows) return fail(DG_ERR_INVALID_VALUE, "ld_sf smaller than rows");
@@ -188,24 +195,101 @@ int dg_quant_1x128(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
   if (!x || !q || !sf) return fail(DG_ERR_INVALID_VALUE, "null pointer argument");
   if (!aligned16(x) || !aligned16(q) || !aligned16(sf)) return fail(DG_ERR_MISALIGNED, "x, q and sf must be 16-byte aligned");
   if (cols == 0 || ld_sf == 0) return ok();
-  const hipError_t e = dg::launch_quant_1x128(x, q, sf, rows, cols, ld_sf, num_groups,
+  const hipError_t e = dg::launch_quant_1x128(x, q, sf, rows, cols, ld_sf, num_groups, pow2,
                                               static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_HIP, "quant_1x128 launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 
-int dg_quant_128x128(const uint16_t* w, uint8_t* q, float* sf, int rows, int cols,
-                     int num_groups, void* stream) {
+int quant_128x128_impl(const uint16_t* w, uint8_t* q, void* sf, int rows, int cols, int num_groups,
+                       bool pow2, void* stream) {
   if (rows < 0 || cols < 0 || num_groups < 1) return fail(DG_ERR_INVALID_VALUE, "bad sizes (rows=%d cols=%d groups=%d)", rows, cols, num_groups);
   if (cols % 128) return fail(DG_ERR_UNSUPPORTED_SHAPE, "cols=%d is not a multiple of 128", cols);
   if (!w || !q || !sf) return fail(DG_ERR_INVALID_VALUE, "null pointer argument");
   if (!aligned16(w) || !aligned16(q) || !aligned16(sf)) return fail(DG_ERR_MISALIGNED, "w, q and sf must be 16-byte aligned");
   if (num_groups > 65535 || (rows + 127) / 128 > 65535) return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many blocks");
   if (rows == 0 || cols == 0) return ok();
-  const hipError_t e = dg::launch_quant_128x128(w, q, sf, rows, cols, num_groups,
+  const hipError_t e = dg::launch_quant_128x128(w, q, sf, rows, cols, num_groups, pow2,
                                                 static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_HIP, "quant_128x128 launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
+                   int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_nt_impl(a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, workspace, workspace_bytes,
+                      stream, false);
+}
+
+int dg_fp8_gemm_nt_ue8m0(const uint8_t* a, const uint8_t* sfa, const uint8_t* b,
+                         const uint8_t* sfb, uint16_t* d, int m, int n, int k, int64_t lda,
+                         int64_t ldb, int64_t ldd, int64_t ld_sfa, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return gemm_nt_impl(a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, workspace, workspace_bytes,
+                      stream, true);
+}
+
+int dg_grouped_contiguous(const uint8_t* a, const float* sfa, const uint8_t* b,
+                          const float* sfb, uint16_t* d, const int32_t* m_indices,
+                          int m_total, int n, int k, int num_groups, int64_t ld_sfa,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return contiguous_impl(a, sfa, b, sfb, d, m_indices, m_total, n, k, num_groups, ld_sfa, workspace,
+                         workspace_bytes, stream, false);
+}
+
+int dg_grouped_contiguous_ue8m0(const uint8_t* a, const uint8_t* sfa, const uint8_t* b,
+                                const uint8_t* sfb, uint16_t* d, const int32_t* m_indices,
+                                int m_total, int n, int k, int num_groups, int64_t ld_sfa,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return contiguous_impl(a, sfa, b, sfb, d, m_indices, m_total, n, k, num_groups, ld_sfa, workspace,
+                         workspace_bytes, stream, true);
+}
+
+int dg_grouped_masked(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                      uint16_t* d, const int32_t* masked_m, int num_groups, int m_max, int n,
+                      int k, int expected_m, int64_t ld_sfa, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return masked_impl(a, sfa, b, sfb, d, masked_m, num_groups, m_max, n, k, expected_m, ld_sfa,
+                     workspace, workspace_bytes, stream, false);
+}
+
+int dg_grouped_masked_ue8m0(const uint8_t* a, const uint8_t* sfa, const uint8_t* b,
+                            const uint8_t* sfb, uint16_t* d, const int32_t* masked_m,
+                            int num_groups, int m_max, int n, int k, int expected_m,
+                            int64_t ld_sfa, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return masked_impl(a, sfa, b, sfb, d, masked_m, num_groups, m_max, n, k, expected_m, ld_sfa,
+                     workspace, workspace_bytes, stream, true);
+}
+
+int dg_quant_1x128(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
+                   int64_t ld_sf, int num_groups, void* stream) {
+  return quant_1x128_impl(x, q, sf, rows, cols, ld_sf, num_groups, false, stream);
+}
+
+int dg_quant_1x128_ue8m0(const uint16_t* x, uint8_t* q, uint8_t* sf, int rows, int cols,
+                         int64_t ld_sf, int num_groups, void* stream) {
+  return quant_1x128_impl(x, q, sf, rows, cols, ld_sf, num_groups, true, stream);
+}
+
+int dg_quant_128x128(const uint16_t* w, uint8_t* q, float* sf, int rows, int cols,
+                     int num_groups, void* stream) {
+  return quant_128x128_impl(w, q, sf, rows, cols, num_groups, false, stream);
+}
+
+int dg_quant_128x128_ue8m0(const uint16_t* w, uint8_t* q, uint8_t* sf, int rows, int cols,
+                           int num_groups, void* stream) {
+  return quant_128x128_impl(w, q, sf, rows, cols, num_groups, true, stream);
+}
+
+int64_t dg_get_ue8m0_sfb_leading_dim(int n) {
+  if (n < 0) return -1;
+  return ((int64_t)(n + 127) / 128 + 3) / 4 * 4;
 }
 
 size_t dg_get_workspace_size(int m, int n, int k, int num_groups) {

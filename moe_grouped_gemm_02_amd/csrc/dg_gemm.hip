@@ -190,7 +190,19 @@ __device__ __forceinline__ void raster(int t, int m_tiles, int n_tiles, int grou
 
 __device__ __forceinline__ int clamp_rows(int v, int hi) { return v < 0 ? 0 : (v > hi ? hi : v); }
 
-template <class T, int LAYOUT, bool SK>
+// Scale formats.  UE8M0 exponents are bytes; the scale pointers keep the
+// fp32 type and group strides count elements of the format in use.
+constexpr int kScaleF32 = 0, kScaleUE8M0 = 1;
+template <int SF>
+__device__ __forceinline__ const float* scale_ptr(const float* base, int64_t offset) {
+  if constexpr (SF == kScaleUE8M0)
+    return reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(base) + offset);
+  return base + offset;
+}
+
+// SF: kScaleF32 (fp32 scales, promoted on the VALU) or kScaleUE8M0 (power-of-
+// two exponents applied inside the block-scaled MFMA, see below).
+template <class T, int LAYOUT, bool SK, int SF>
 __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedule s) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::STAGES * T::kStageBytes];
   __shared__ int last_flag;
@@ -302,7 +314,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
     if (LAYOUT == kMasked) {
       rows_valid = clamp_rows(p.masked_m[g], p.m);
       A += (int64_t)g * p.a_gstride;
-      SA += (int64_t)g * p.sfa_gstride;
+      SA = scale_ptr<SF>(SA, (int64_t)g * p.sfa_gstride);
       D += (int64_t)g * p.d_gstride;
     }
     // Contiguous layout: the experts of the tile's 128-row halves.  A tile
@@ -336,7 +348,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
     for (int pass = 0; pass < passes; ++pass) {
       if (LAYOUT == kContiguous) g = __builtin_amdgcn_readfirstlane(pass == 0 ? pass_group[0] : pass_group[1]);
       const uint8_t* B = uniform_ptr(p.b + (int64_t)g * p.b_gstride);
-      const float* SB = uniform_ptr(p.sfb + (int64_t)g * p.sfb_gstride);
+      const float* SB = uniform_ptr(scale_ptr<SF>(p.sfb, (int64_t)g * p.sfb_gstride));
       const int nkb = kb1 - kb0;
       // K walk order.  With k_rotate the tile visits its slices starting at
       // (tile mod slices) and wraps, so workgroups running at the same time
@@ -377,15 +389,29 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
           const int gn = min(n0 + r, p.n - 1);
           dma16(stage_lds + instr * 1024, B, (uint32_t)gn * (uint32_t)p.ldb + kb * 128 + c * 16);
         } else {
-          if (wave == 0) {
-            // Activation scales of the slice: rows m0 .. m0 + 4*63 + 3.
-            const int r4 = min(m0 + 4 * lane, (int)p.ld_sfa - 4);
-            dma16(stage_lds + T::kSOffInstr * 1024, SA, (uint32_t)(kb * p.ld_sfa + r4) * 4u);
-          } else if (wave == 1) {
-            // Weight scales of the slice for the tile's column blocks (lane l:
-            // block cb_first + l; lanes past the last block repeat it).
-            const int cb = cb_first + min(lane, cb_count - 1);
-            dma4(stage_lds + T::kSBOff, SB, (uint32_t)(cb * nkb_total + kb) * 4u);
+          if constexpr (SF == kScaleUE8M0) {
+            // Exponent bytes, MN-major for both operands (four to a dword).
+            if (wave == 0) {
+              // rows m0 .. m0 + BM - 1 of the slice: lane l takes rows
+              // m0 + 4l .. m0 + 4l + 3 (never clamped for a valid row).
+              const int r4 = min(m0 + 4 * lane, (int)p.ld_sfa - 4);
+              dma4(stage_lds + T::kSOffInstr * 1024, SA, (uint32_t)(kb * p.ld_sfa + r4));
+            } else if (wave == 1) {
+              // column blocks (cb_first & ~3) .. + 7 of the slice (lanes 0, 1).
+              const int c4 = min((cb_first & ~3) + 4 * min(lane, 1), (int)p.ld_sfb - 4);
+              dma4(stage_lds + T::kSBOff, SB, (uint32_t)(kb * p.ld_sfb + c4));
+            }
+          } else {
+            if (wave == 0) {
+              // Activation scales of the slice: rows m0 .. m0 + 4*63 + 3.
+              const int r4 = min(m0 + 4 * lane, (int)p.ld_sfa - 4);
+              dma16(stage_lds + T::kSOffInstr * 1024, SA, (uint32_t)(kb * p.ld_sfa + r4) * 4u);
+            } else if (wave == 1) {
+              // Weight scales of the slice for the tile's column blocks (lane l:
+              // block cb_first + l; lanes past the last block repeat it).
+              const int cb = cb_first + min(lane, cb_count - 1);
+              dma4(stage_lds + T::kSBOff, SB, (uint32_t)(cb * nkb_total + kb) * 4u);
+            }
           }
         }
       };
@@ -436,79 +462,123 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
         }
 
         const uint8_t* st = smem + (it % T::STAGES) * T::kStageBytes;
-        float sbw = 0.0f;
-        float sbv[T::FN];
-        const float* sbs = reinterpret_cast<const float*>(st + T::kSBOff);
-        if (T::kOneSB) {
-          const int cb = min((n0 + wn * T::TN) >> 7, n_blocks - 1);
-          sbw = sbs[cb - cb_first];
-        } else {
-#pragma unroll
-          for (int j = 0; j < T::FN; ++j) {
-            const int cb = min((n0 + wn * T::TN + j * 16) >> 7, n_blocks - 1);
-            sbv[j] = sbs[cb - cb_first];
-          }
-        }
-        v8i bfrag[T::FN];
-#pragma unroll
-        for (int j = 0; j < T::FN; ++j) {
-          const uint8_t* rowp = st + T::kBOff + (wn * T::TN + j * 16 + fr) * 128;
-          bfrag[j] = make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
-                              *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
-        }
-        // Software pipeline over the fragment rows: the MFMAs of row i+1 are
-        // issued into a second set of result registers before the promotion
-        // FMAs of row i, so the matrix core and the VALU overlap instead of
-        // each FMA waiting on the MFMA just issued.
-        auto load_a = [&](int i) {
-          const uint8_t* rowp = st + (wm * T::TM + i * 16 + fr) * 128;
-          return make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
-                          *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
-        };
-        auto load_s = [&](int i) {
-          return *reinterpret_cast<const float4*>(st + T::kSOff + (wm * T::TM + i * 16 + 4 * kg) * 4);
-        };
-        v4f part[T::kPipe ? 2 : 1][T::FN];
-        v8i afrag = load_a(0);
-        float4 s4 = load_s(0);
-        if (T::kPipe) {
-#pragma unroll
-          for (int j = 0; j < T::FN; ++j) part[0][j] = mfma_fp8_slice(afrag, bfrag[j]);
-        }
-        static_for<T::FM>([&](auto ic) {
-          constexpr int i = decltype(ic)::value;
-          constexpr int cur = T::kPipe ? (i & 1) : 0;
-          const float4 s_cur = s4;
-          if constexpr (T::kPipe) {
-            if constexpr (i + 1 < T::FM) {
-              afrag = load_a(i + 1);
-              s4 = load_s(i + 1);
-#pragma unroll
-              for (int j = 0; j < T::FN; ++j) part[cur ^ 1][j] = mfma_fp8_slice(afrag, bfrag[j]);
-            }
-          } else {
-            // MFMAs of row i, then the LDS reads of row i + 1, which complete
-            // while the promotion FMAs of row i run.
-#pragma unroll
-            for (int j = 0; j < T::FN; ++j) part[0][j] = mfma_fp8_slice(afrag, bfrag[j]);
-            if constexpr (i + 1 < T::FM) {
-              afrag = load_a(i + 1);
-              s4 = load_s(i + 1);
-            }
-          }
-          if constexpr (T::kSpreadRows > 0) {
-            if (refill) issue_row(kb_next, buf_next, ic);
-          }
-          const float sa[4] = {s_cur.x, s_cur.y, s_cur.z, s_cur.w};
-          float sc[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sc[e] = T::kOneSB ? sa[e] * sbw : 0.0f;
+        if constexpr (SF == kScaleUE8M0) {
+          // Block-scaled MFMA: lane l supplies the exponent of its A row
+          // (l % 16) and of its B column (l % 16) for the 32-deep K block
+          // l / 16; all four blocks of a slice share the 128-wide scales, and
+          // the products, scaled by 2^(ea + eb - 254), accumulate into acc
+          // inside the matrix core.  No promotion on the VALU.
+          const uint8_t* sbb = st + T::kSBOff - (cb_first & ~3);
+          int sbe[T::FN];
 #pragma unroll
           for (int j = 0; j < T::FN; ++j)
+            sbe[j] = sbb[min((n0 + wn * T::TN + j * 16) >> 7, n_blocks - 1)];
+          v8i bfrag[T::FN];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[i][j][e] = fmaf(part[cur][j][e], T::kOneSB ? sc[e] : sa[e] * sbv[j], acc[i][j][e]);
-        });
+          for (int j = 0; j < T::FN; ++j) {
+            const uint8_t* rowp = st + T::kBOff + (wn * T::TN + j * 16 + fr) * 128;
+            bfrag[j] = make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
+                                *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
+          }
+          auto load_a = [&](int i) {
+            const uint8_t* rowp = st + (wm * T::TM + i * 16 + fr) * 128;
+            return make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
+                            *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
+          };
+          auto load_e = [&](int i) { return (int)st[T::kSOff + wm * T::TM + i * 16 + fr]; };
+          v8i afrag = load_a(0);
+          int ae = load_e(0);
+          static_for<T::FM>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            const v8i a_cur = afrag;
+            const int e_cur = ae;
+            if constexpr (i + 1 < T::FM) {
+              afrag = load_a(i + 1);
+              ae = load_e(i + 1);
+            }
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_cur, bfrag[j], acc[i][j], 0, 0, 0, e_cur,
+                                                                           0, sbe[j]);
+            if constexpr (T::kSpreadRows > 0) {
+              if (refill) issue_row(kb_next, buf_next, ic);
+            }
+          });
+        } else {
+          float sbw = 0.0f;
+          float sbv[T::FN];
+          const float* sbs = reinterpret_cast<const float*>(st + T::kSBOff);
+          if (T::kOneSB) {
+            const int cb = min((n0 + wn * T::TN) >> 7, n_blocks - 1);
+            sbw = sbs[cb - cb_first];
+          } else {
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j) {
+              const int cb = min((n0 + wn * T::TN + j * 16) >> 7, n_blocks - 1);
+              sbv[j] = sbs[cb - cb_first];
+            }
+          }
+          v8i bfrag[T::FN];
+#pragma unroll
+          for (int j = 0; j < T::FN; ++j) {
+            const uint8_t* rowp = st + T::kBOff + (wn * T::TN + j * 16 + fr) * 128;
+            bfrag[j] = make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
+                                *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
+          }
+          // Software pipeline over the fragment rows: the MFMAs of row i+1 are
+          // issued into a second set of result registers before the promotion
+          // FMAs of row i, so the matrix core and the VALU overlap instead of
+          // each FMA waiting on the MFMA just issued.
+          auto load_a = [&](int i) {
+            const uint8_t* rowp = st + (wm * T::TM + i * 16 + fr) * 128;
+            return make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
+                            *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
+          };
+          auto load_s = [&](int i) {
+            return *reinterpret_cast<const float4*>(st + T::kSOff + (wm * T::TM + i * 16 + 4 * kg) * 4);
+          };
+          v4f part[T::kPipe ? 2 : 1][T::FN];
+          v8i afrag = load_a(0);
+          float4 s4 = load_s(0);
+          if (T::kPipe) {
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j) part[0][j] = mfma_fp8_slice(afrag, bfrag[j]);
+          }
+          static_for<T::FM>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            constexpr int cur = T::kPipe ? (i & 1) : 0;
+            const float4 s_cur = s4;
+            if constexpr (T::kPipe) {
+              if constexpr (i + 1 < T::FM) {
+                afrag = load_a(i + 1);
+                s4 = load_s(i + 1);
+#pragma unroll
+                for (int j = 0; j < T::FN; ++j) part[cur ^ 1][j] = mfma_fp8_slice(afrag, bfrag[j]);
+              }
+            } else {
+              // MFMAs of row i, then the LDS reads of row i + 1, which complete
+              // while the promotion FMAs of row i run.
+#pragma unroll
+              for (int j = 0; j < T::FN; ++j) part[0][j] = mfma_fp8_slice(afrag, bfrag[j]);
+              if constexpr (i + 1 < T::FM) {
+                afrag = load_a(i + 1);
+                s4 = load_s(i + 1);
+              }
+            }
+            if constexpr (T::kSpreadRows > 0) {
+              if (refill) issue_row(kb_next, buf_next, ic);
+            }
+            const float sa[4] = {s_cur.x, s_cur.y, s_cur.z, s_cur.w};
+            float sc[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc[e] = T::kOneSB ? sa[e] * sbw : 0.0f;
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                acc[i][j][e] = fmaf(part[cur][j][e], T::kOneSB ? sc[e] : sa[e] * sbv[j], acc[i][j][e]);
+          });
+        }
       }
 
       // ------------------------------------------------------- split-K fixup
@@ -669,24 +739,24 @@ constexpr Variant kVariants[] = {
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-template <class T, int LAYOUT>
+template <class T, int LAYOUT, int SF>
 hipError_t launch_one(const GemmParams& p, const Schedule& s, int grid, hipStream_t stream) {
   if constexpr (LAYOUT != kContiguous) {  // contiguous tiles may take two passes: data-parallel only
     if (s.stream_k) {
-      hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
+      hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, true, SF>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, false>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
+  hipLaunchKernelGGL((gemm_kernel<T, LAYOUT, false, SF>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
   return hipGetLastError();
 }
 
-template <class T>
+template <class T, int SF>
 hipError_t launch_layout(int layout, const GemmParams& p, const Schedule& s, int grid, hipStream_t stream) {
   switch (layout) {
-    case kDense: return launch_one<T, kDense>(p, s, grid, stream);
-    case kContiguous: return launch_one<T, kContiguous>(p, s, grid, stream);
-    default: return launch_one<T, kMasked>(p, s, grid, stream);
+    case kDense: return launch_one<T, kDense, SF>(p, s, grid, stream);
+    case kContiguous: return launch_one<T, kContiguous, SF>(p, s, grid, stream);
+    default: return launch_one<T, kMasked, SF>(p, s, grid, stream);
   }
 }
 
@@ -818,18 +888,27 @@ hipError_t launch_gemm(int layout, const GemmParams& p0, const GemmConfig& cfg,
   if (cfg.stream_k)
     p.counters = reinterpret_cast<int*>(reinterpret_cast<char*>(p.workspace) +
                                         2 * (size_t)cfg.sk_slots * cfg.bm * cfg.bn * sizeof(float));
+  if (p.sf_ue8m0) {  // UE8M0 instances: the tiles the heuristic picks
+    switch (cfg.variant) {
+      case 0: return launch_layout<TileP256, kScaleUE8M0>(layout, p, s, cfg.grid, stream);
+      case 1: return launch_layout<TileP128, kScaleUE8M0>(layout, p, s, cfg.grid, stream);
+      case 4: return launch_layout<TileS64, kScaleUE8M0>(layout, p, s, cfg.grid, stream);
+      case 6: return launch_layout<TileP128w8, kScaleUE8M0>(layout, p, s, cfg.grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (cfg.variant) {
-    case 0: return launch_layout<TileP256>(layout, p, s, cfg.grid, stream);
-    case 1: return launch_layout<TileP128>(layout, p, s, cfg.grid, stream);
-    case 2: return launch_layout<TileD128>(layout, p, s, cfg.grid, stream);
-    case 3: return launch_layout<TileD64>(layout, p, s, cfg.grid, stream);
-    case 4: return launch_layout<TileS64>(layout, p, s, cfg.grid, stream);
-    case 5: return launch_layout<TileW128>(layout, p, s, cfg.grid, stream);
-    case 6: return launch_layout<TileP128w8>(layout, p, s, cfg.grid, stream);
-    case 7: return launch_layout<TileS64w8>(layout, p, s, cfg.grid, stream);
-    case 8: return launch_layout<TileW128w16>(layout, p, s, cfg.grid, stream);
-    case 9: return launch_layout<TileV128>(layout, p, s, cfg.grid, stream);
-    default: return launch_layout<TileV128w8>(layout, p, s, cfg.grid, stream);
+    case 0: return launch_layout<TileP256, kScaleF32>(layout, p, s, cfg.grid, stream);
+    case 1: return launch_layout<TileP128, kScaleF32>(layout, p, s, cfg.grid, stream);
+    case 2: return launch_layout<TileD128, kScaleF32>(layout, p, s, cfg.grid, stream);
+    case 3: return launch_layout<TileD64, kScaleF32>(layout, p, s, cfg.grid, stream);
+    case 4: return launch_layout<TileS64, kScaleF32>(layout, p, s, cfg.grid, stream);
+    case 5: return launch_layout<TileW128, kScaleF32>(layout, p, s, cfg.grid, stream);
+    case 6: return launch_layout<TileP128w8, kScaleF32>(layout, p, s, cfg.grid, stream);
+    case 7: return launch_layout<TileS64w8, kScaleF32>(layout, p, s, cfg.grid, stream);
+    case 8: return launch_layout<TileW128w16, kScaleF32>(layout, p, s, cfg.grid, stream);
+    case 9: return launch_layout<TileV128, kScaleF32>(layout, p, s, cfg.grid, stream);
+    default: return launch_layout<TileV128w8, kScaleF32>(layout, p, s, cfg.grid, stream);
   }
 }
 

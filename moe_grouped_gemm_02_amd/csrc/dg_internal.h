@@ -25,7 +25,15 @@ struct GemmParams {
   int num_groups;
   int64_t lda, ldb, ldd, ld_sfa;
   int64_t a_gstride, sfa_gstride, b_gstride, sfb_gstride, d_gstride;
+  // UE8M0 scales (power-of-two exponent bytes): sfa/sfb point at bytes, the
+  // weight exponents are MN-major [G][K/128][ld_sfb], and the scale group
+  // strides count bytes.
+  int sf_ue8m0;
+  int64_t ld_sfb;
 };
+
+// Tile variants built with UE8M0 scales.
+inline bool ue8m0_variant_built(int variant) { return variant == 0 || variant == 1 || variant == 4 || variant == 6; }
 
 // Tile configuration chosen on the host (deterministically, from the shape).
 struct GemmConfig {
@@ -60,9 +68,10 @@ size_t workspace_bytes_for(const GemmConfig& cfg, int layout, int m, int n, int 
 
 hipError_t launch_gemm(int layout, const GemmParams& p, const GemmConfig& cfg,
                        hipStream_t stream);
-hipError_t launch_quant_1x128(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
-                              int64_t ld_sf, int groups, hipStream_t stream);
-hipError_t launch_quant_128x128(const uint16_t* w, uint8_t* q, float* sf, int rows, int cols,
-                                int groups, hipStream_t stream);
+// pow2: UE8M0 exponent bytes instead of fp32 scales (see dg_quant.hip).
+hipError_t launch_quant_1x128(const uint16_t* x, uint8_t* q, void* sf, int rows, int cols,
+                              int64_t ld_sf, int groups, bool pow2, hipStream_t stream);
+hipError_t launch_quant_128x128(const uint16_t* w, uint8_t* q, void* sf, int rows, int cols,
+                                int groups, bool pow2, hipStream_t stream);
 
 }  // namespace dg

@@ -42,15 +42,41 @@ __device__ __forceinline__ uint32_t e4m3_x4(float a, float b, float c, float d) 
   return (uint32_t)w;
 }
 
+// Power-of-two (UE8M0) scales: E = ceil(log2(amax / 448)) + 127, clamped to
+// [0, 254], 0 for an all-zero tile; the scale is 2^(E - 127).  The quotient
+// amax/448 is formed in fp64: for a bf16 amax it is either exactly a power of
+// two (amax = 7 * 2^j) or at least 2^-11 (relative) away from one, so the
+// fp64 rounding cannot move it across a power of two.
+__device__ __forceinline__ uint32_t ue8m0_exponent(float amax) {
+  if (amax == 0.0f) return 0u;
+  const double v = (double)amax / 448.0;
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  int e = (int)((u >> 52) & 0x7FF) - 1023;  // v is a normal fp64 number
+  if (u & 0xFFFFFFFFFFFFFull) e += 1;       // not a power of two: round up
+  e += 127;
+  return (uint32_t)(e < 0 ? 0 : (e > 254 ? 254 : e));
+}
+
+// x / 2^(E - 127): exact in fp32 except below the normal range, where
+// v_ldexp_f32 rounds to nearest even.
+__device__ __forceinline__ float pow2_quotient(uint32_t bf16_bits, uint32_t e) {
+  return __builtin_ldexpf(bf16_bits_to_f32(bf16_bits), 127 - (int)e);
+}
+
 // 1x128 activation tiles.  Block (x, y) covers tiles [32 x, 32 x + 32) of the
 // rows y, y + gridDim.y, ...; 8 consecutive lanes own one tile, 16 bf16
 // values (32 bytes) each, so a wave reads 2 KB of one row.
 constexpr int kQTilesPerBlock = 32;
 
+// POW2: scales are UE8M0 exponents (one byte each) instead of fp32 values;
+// the scale matrices have the same [(G)][C/128][ld] shape either way.
+template <bool POW2>
 __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __restrict__ x,
                                                           uint8_t* __restrict__ q,
-                                                          float* __restrict__ sf, int rows,
+                                                          void* __restrict__ sf_out, int rows,
                                                           int cols, int64_t ld_sf, int groups) {
+  float* sf = static_cast<float*>(sf_out);
+  uint8_t* sf8 = static_cast<uint8_t*>(sf_out);
   const int tiles_per_row = cols / kBlockK;
   const int total_rows = groups * rows;
   const int sub = threadIdx.x & 7;  // lane within the tile's 8-lane group
@@ -68,15 +94,25 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __rest
         amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w[i] & 0xFFFFu)), fabsf(bf16_bits_to_f32(w[i] >> 16))));
 #pragma unroll
       for (int off = 4; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 8));
-      const float s = amax / 448.0f;
-      const double rcp = tile_reciprocal(s);
       uint32_t out[4];
+      const int64_t sf_at = ((int64_t)g * tiles_per_row + j) * ld_sf + r;
+      if constexpr (POW2) {
+        const uint32_t e = ue8m0_exponent(amax);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        out[i] = e4m3_x4(quotient(w[2 * i] & 0xFFFFu, rcp), quotient(w[2 * i] >> 16, rcp),
-                         quotient(w[2 * i + 1] & 0xFFFFu, rcp), quotient(w[2 * i + 1] >> 16, rcp));
+        for (int i = 0; i < 4; ++i)
+          out[i] = e4m3_x4(pow2_quotient(w[2 * i] & 0xFFFFu, e), pow2_quotient(w[2 * i] >> 16, e),
+                           pow2_quotient(w[2 * i + 1] & 0xFFFFu, e), pow2_quotient(w[2 * i + 1] >> 16, e));
+        if (sub == 0) sf8[sf_at] = (uint8_t)e;
+      } else {
+        const float s = amax / 448.0f;
+        const double rcp = tile_reciprocal(s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          out[i] = e4m3_x4(quotient(w[2 * i] & 0xFFFFu, rcp), quotient(w[2 * i] >> 16, rcp),
+                           quotient(w[2 * i + 1] & 0xFFFFu, rcp), quotient(w[2 * i + 1] >> 16, rcp));
+        if (sub == 0) sf[sf_at] = s;
+      }
       *reinterpret_cast<uint4*>(q + elem) = make_uint4(out[0], out[1], out[2], out[3]);
-      if (sub == 0) sf[((int64_t)g * tiles_per_row + j) * ld_sf + r] = s;
     }
   }
   // Padding entries of the scale matrix (rows in [rows, ld_sf)) are zero.
@@ -86,17 +122,23 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __rest
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < pads;
          i += (int64_t)gridDim.x * blockDim.x) {
       const int64_t col = i / pad;  // g * tiles_per_row + j
-      sf[col * ld_sf + rows + (i % pad)] = 0.0f;
+      if constexpr (POW2) sf8[col * ld_sf + rows + (i % pad)] = 0;
+      else sf[col * ld_sf + rows + (i % pad)] = 0.0f;
     }
   }
 }
 
 // One 128x128 block per workgroup of 256 threads: 2048 16-byte chunks, 8 per
 // thread, held in registers between the amax reduction and the encode.
+// POW2: UE8M0 exponents in an MN-major [G][K/128][ld_n] byte matrix,
+// ld_n = round_up(ceil(N/128), 4), instead of fp32 [G][ceil(N/128)][K/128].
+template <bool POW2>
 __global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __restrict__ w,
                                                             uint8_t* __restrict__ q,
-                                                            float* __restrict__ sf, int rows,
+                                                            void* __restrict__ sf_out, int rows,
                                                             int cols) {
+  float* sf = static_cast<float*>(sf_out);
+  uint8_t* sf8 = static_cast<uint8_t*>(sf_out);
   __shared__ float wave_max[4];
   const int kb = blockIdx.x, nb = blockIdx.y, g = blockIdx.z;
   const int kblocks = cols / kBlockK;
@@ -127,23 +169,30 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __re
   amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
   const float s = amax / 448.0f;
   const double rcp = tile_reciprocal(s);
-  if (tid == 0) sf[((int64_t)g * nblocks + nb) * kblocks + kb] = s;
+  const uint32_t e = POW2 ? ue8m0_exponent(amax) : 0u;
+  if constexpr (POW2) {
+    const int ld_n = (nblocks + 3) / 4 * 4;
+    uint8_t* col = sf8 + ((int64_t)g * kblocks + kb) * ld_n;
+    if (tid == 0) col[nb] = (uint8_t)e;
+    if (nb == nblocks - 1 && tid >= 1 && tid < 4 && nb + tid < ld_n) col[nb + tid] = 0;  // pads
+  } else {
+    if (tid == 0) sf[((int64_t)g * nblocks + nb) * kblocks + kb] = s;
+  }
+  auto quo = [&](uint32_t bits) { return POW2 ? pow2_quotient(bits, e) : quotient(bits, rcp); };
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = nb * kBlockK + (tid >> 4) + 16 * i;
     if (r >= rows) continue;
     const uint32_t p[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
-    const uint32_t lo = e4m3_x4(quotient(p[0] & 0xFFFFu, rcp), quotient(p[0] >> 16, rcp),
-                                quotient(p[1] & 0xFFFFu, rcp), quotient(p[1] >> 16, rcp));
-    const uint32_t hi = e4m3_x4(quotient(p[2] & 0xFFFFu, rcp), quotient(p[2] >> 16, rcp),
-                                quotient(p[3] & 0xFFFFu, rcp), quotient(p[3] >> 16, rcp));
+    const uint32_t lo = e4m3_x4(quo(p[0] & 0xFFFFu), quo(p[0] >> 16), quo(p[1] & 0xFFFFu), quo(p[1] >> 16));
+    const uint32_t hi = e4m3_x4(quo(p[2] & 0xFFFFu), quo(p[2] >> 16), quo(p[3] & 0xFFFFu), quo(p[3] >> 16));
     *reinterpret_cast<uint2*>(q + base + (int64_t)r * cols + kb * kBlockK + chunk * 8) =
         make_uint2(lo, hi);
   }
 }
 
-hipError_t launch_quant_1x128(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
-                              int64_t ld_sf, int groups, hipStream_t stream) {
+hipError_t launch_quant_1x128(const uint16_t* x, uint8_t* q, void* sf, int rows, int cols,
+                              int64_t ld_sf, int groups, bool pow2, hipStream_t stream) {
   const int tiles_per_row = cols / kBlockK;
   const int gx = (tiles_per_row + kQTilesPerBlock - 1) / kQTilesPerBlock;
   const int64_t total_rows = (int64_t)groups * rows;
@@ -152,15 +201,21 @@ hipError_t launch_quant_1x128(const uint16_t* x, uint8_t* q, float* sf, int rows
   if (gy > total_rows) gy = total_rows;
   if (gy > 65535) gy = 65535;
   if (gy < 1) gy = 1;
-  hipLaunchKernelGGL(quant_1x128_kernel, dim3(gx > 0 ? gx : 1, (unsigned)gy), dim3(256), 0, stream, x, q,
-                     sf, rows, cols, ld_sf, groups);
+  const dim3 grid(gx > 0 ? gx : 1, (unsigned)gy);
+  if (pow2)
+    hipLaunchKernelGGL(quant_1x128_kernel<true>, grid, dim3(256), 0, stream, x, q, sf, rows, cols, ld_sf, groups);
+  else
+    hipLaunchKernelGGL(quant_1x128_kernel<false>, grid, dim3(256), 0, stream, x, q, sf, rows, cols, ld_sf, groups);
   return hipGetLastError();
 }
 
-hipError_t launch_quant_128x128(const uint16_t* w, uint8_t* q, float* sf, int rows, int cols,
-                                int groups, hipStream_t stream) {
+hipError_t launch_quant_128x128(const uint16_t* w, uint8_t* q, void* sf, int rows, int cols,
+                                int groups, bool pow2, hipStream_t stream) {
   const dim3 grid(cols / kBlockK, (rows + kBlockK - 1) / kBlockK, groups);
-  hipLaunchKernelGGL(quant_128x128_kernel, grid, dim3(256), 0, stream, w, q, sf, rows, cols);
+  if (pow2)
+    hipLaunchKernelGGL(quant_128x128_kernel<true>, grid, dim3(256), 0, stream, w, q, sf, rows, cols);
+  else
+    hipLaunchKernelGGL(quant_128x128_kernel<false>, grid, dim3(256), 0, stream, w, q, sf, rows, cols);
   return hipGetLastError();
 }
 

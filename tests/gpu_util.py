@@ -59,3 +59,28 @@ def gpu_quant_128x128(dg, w_bits):
     sf = torch.full(sf_shape, float("nan"), dtype=torch.float32, device="cuda")
     dg.dg_quant_128x128(w, q, sf)
     return q, sf
+
+
+def gpu_quant_1x128_ue8m0(dg, x_bits, ld=None):
+    x = dev(x_bits)
+    shape = x_bits.shape
+    rows, cols = shape[-2], shape[-1]
+    ld = dg.dg_get_sf_leading_dim(rows) if ld is None else ld
+    q = torch.empty(shape, dtype=torch.uint8, device="cuda")
+    sf_shape = (cols // 128, ld) if len(shape) == 2 else (shape[0], cols // 128, ld)
+    sf = torch.full(sf_shape, 0xEE, dtype=torch.uint8, device="cuda")
+    dg.dg_quant_1x128_ue8m0(x, q, sf)
+    return q, sf
+
+
+def gpu_quant_128x128_ue8m0(dg, w_bits):
+    w = dev(w_bits)
+    shape = w_bits.shape
+    rows, cols = shape[-2], shape[-1]
+    sf_shape = (cols // 128, dg.dg_get_ue8m0_sfb_leading_dim(rows))
+    if len(shape) == 3:
+        sf_shape = (shape[0],) + sf_shape
+    q = torch.empty(shape, dtype=torch.uint8, device="cuda")
+    sf = torch.full(sf_shape, 0xEE, dtype=torch.uint8, device="cuda")
+    dg.dg_quant_128x128_ue8m0(w, q, sf)
+    return q, sf
