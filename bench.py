@@ -72,8 +72,9 @@ def algorithmic_bytes(m_valid, n, k, groups=1):
     return float(m_valid * k + groups * n * k + 2 * m_valid * n)
 
 
-def scale_bytes(m_valid, n, k, groups=1):
-    return float(4 * m_valid * (k // 128) + 4 * groups * ((n + 127) // 128) * (k // 128))
+def scale_bytes(m_valid, n, k, groups=1, scales="fp32"):
+    per = 1 if scales == "ue8m0" else 4
+    return float(per * m_valid * (k // 128) + per * groups * ((n + 127) // 128) * (k // 128))
 
 
 def parse_args(argv=None):
@@ -83,6 +84,8 @@ def parse_args(argv=None):
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="decode128",
                    help="decode128 (default) | all | a workload name from synth.workloads()")
+    p.add_argument("--scales", choices=("fp32", "ue8m0"), default="fp32",
+                   help="scale format: fp32 (default) or power-of-two exponent bytes (UE8M0)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work for the oracle sample")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -119,9 +122,12 @@ def select_workloads(name):
 class Prepared:
     """Device buffers for one workload shape, weights rotated for cache misses."""
 
-    def __init__(self, dg, torch, wl):
+    def __init__(self, dg, torch, wl, scales="fp32"):
         import synth
         self.wl = wl
+        self.scales = scales
+        ue = scales == "ue8m0"
+        sf_dtype = torch.uint8 if ue else torch.float32
         g, n, k = wl.groups, wl.n, wl.k
         dev = "cuda"
         if wl.layout == "dense":
@@ -134,14 +140,15 @@ class Prepared:
         self.x = torch.from_numpy(xa.view(np.int16)).to(dev)
         self.a = torch.empty(a_shape, dtype=torch.uint8, device=dev)
         ld = dg.dg_get_sf_leading_dim(self.m_rows)
-        self.sfa = torch.empty(((g,) if wl.layout == "masked" else ()) + (k // 128, ld), dtype=torch.float32, device=dev)
+        self.sfa = torch.empty(((g,) if wl.layout == "masked" else ()) + (k // 128, ld), dtype=sf_dtype, device=dev)
         b_shape = (n, k) if wl.layout == "dense" else (g, n, k)
         xb = torch.from_numpy(synth.bf16_normal(b_shape, wl.seed_b).view(np.int16)).to(dev)
         qb = torch.empty(b_shape, dtype=torch.uint8, device=dev)
-        sfb = torch.empty(((g,) if wl.layout != "dense" else ()) + ((n + 127) // 128, k // 128), dtype=torch.float32, device=dev)
-        dg.dg_quant_128x128(xb, qb, sfb)
+        sfb_shape = (k // 128, dg.dg_get_ue8m0_sfb_leading_dim(n)) if ue else ((n + 127) // 128, k // 128)
+        sfb = torch.empty(((g,) if wl.layout != "dense" else ()) + sfb_shape, dtype=sf_dtype, device=dev)
+        (dg.dg_quant_128x128_ue8m0 if ue else dg.dg_quant_128x128)(xb, qb, sfb)
         del xb
-        set_bytes = qb.numel() + sfb.numel() * 4
+        set_bytes = qb.numel() + sfb.numel() * sfb.element_size()
         copies = max(1, math.ceil(2 * MALL_BYTES / set_bytes)) if set_bytes < 2 * MALL_BYTES else 1
         copies = min(copies, 64)
         self.b = [qb] + [qb.clone() for _ in range(copies - 1)]
@@ -162,7 +169,7 @@ class Prepared:
         self.ws = torch.zeros(ws, dtype=torch.uint8, device=dev) if ws else None
         self.flops = algorithmic_flops(self.m_valid, n, k)
         self.bytes = algorithmic_bytes(self.m_valid, n, k, g)
-        self.sf_bytes = scale_bytes(self.m_valid, n, k, g)
+        self.sf_bytes = scale_bytes(self.m_valid, n, k, g, scales)
         layout_id = {"dense": 0, "contiguous": 1, "masked": 2}[wl.layout]
         self.expected_m = self.m_valid // g if wl.layout == "masked" else 0
         self.config = dg.dg_describe_config(layout_id, self.m_rows, n, k, g, dg.dg_get_num_cus(), self.expected_m)
@@ -170,20 +177,23 @@ class Prepared:
         # unit rocprofv3 reports durations for.
         fields = dict(kv.split("=") for kv in self.config.split())
         self.kernel_key = (f"gemm_kernel variant={fields['variant']} bm={fields['bm']} bn={fields['bn']} "
-                           f"layout={wl.layout} stream_k={fields['stream_k']}")
+                           f"layout={wl.layout} stream_k={fields['stream_k']} scales={scales}")
+        sfx = "_ue8m0" if ue else ""
+        self._quant_a = getattr(dg, "dg_quant_1x128" + sfx)
+        self._gemm = getattr(dg, {"dense": "dg_fp8_gemm_nt", "contiguous": "dg_grouped_contiguous",
+                                  "masked": "dg_grouped_masked"}[wl.layout] + sfx)
 
     def quant(self, dg):
-        dg.dg_quant_1x128(self.x, self.a, self.sfa)
+        self._quant_a(self.x, self.a, self.sfa)
 
     def gemm(self, dg, r):
         b, sfb = self.b[r % len(self.b)], self.sfb[r % len(self.sfb)]
         if self.wl.layout == "dense":
-            dg.dg_fp8_gemm_nt(self.a, self.sfa, b, sfb, self.d, workspace=self.ws)
+            self._gemm(self.a, self.sfa, b, sfb, self.d, workspace=self.ws)
         elif self.wl.layout == "contiguous":
-            dg.dg_grouped_contiguous(self.a, self.sfa, b, sfb, self.d, self.mi, workspace=self.ws)
+            self._gemm(self.a, self.sfa, b, sfb, self.d, self.mi, workspace=self.ws)
         else:
-            dg.dg_grouped_masked(self.a, self.sfa, b, sfb, self.d, self.mm, expected_m=self.expected_m,
-                                 workspace=self.ws)
+            self._gemm(self.a, self.sfa, b, sfb, self.d, self.mm, expected_m=self.expected_m, workspace=self.ws)
 
 
 # ------------------------------------------------------------------ timing --
@@ -312,7 +322,7 @@ def time_quant(dg, torch, p, reps=20):
 
 # ------------------------------------------------------------ CPU baseline --
 
-def cpu_baseline(wls, target_s):
+def cpu_baseline(wls, target_s, scales="fp32"):
     """The oracle, single-threaded, on a bounded sample of the workload.
 
     Sample: for each shape, all M rows of A (at most 256) against the first
@@ -323,15 +333,26 @@ def cpu_baseline(wls, target_s):
     Rate = sample flops / oracle seconds.
     """
     import synth
-    from oracle import gemm, quant
+    from oracle import gemm, quant, ue8m0
     from threadpoolctl import threadpool_limits
+
+    if scales == "ue8m0":
+        def quant_b(xb):
+            qb, eb = ue8m0.quant_128x128_ue8m0(xb)
+            return qb, ue8m0.sfb_as_fp32(eb, xb.shape[0])
+
+        def quant_a(xa):
+            qa, ea = ue8m0.quant_1x128_ue8m0(xa)
+            return qa, ue8m0.sfa_as_fp32(ea)
+    else:
+        quant_b, quant_a = quant.quant_128x128, quant.quant_1x128
 
     samples = []
     for wl in wls:
         m = wl.m if wl.layout == "dense" else min(wl.m, 256)
         ncols = min(wl.n, 1024)
         xa = synth.bf16_normal((m, wl.k), wl.seed_a)
-        qb, sfb = quant.quant_128x128(synth.bf16_normal((ncols, wl.k), wl.seed_b))
+        qb, sfb = quant_b(synth.bf16_normal((ncols, wl.k), wl.seed_b))
         samples.append((wl, m, ncols, xa, qb, sfb))
     flops = 0.0
     secs = 0.0
@@ -340,7 +361,7 @@ def cpu_baseline(wls, target_s):
         while secs < target_s and runs < 20 * len(samples):
             wl, m, ncols, xa, qb, sfb = samples[runs % len(samples)]
             t0 = time.perf_counter()
-            qa, sfa = quant.quant_1x128(xa)
+            qa, sfa = quant_a(xa)
             gemm.gemm_nt_ref(qa, sfa, qb, sfb)
             secs += time.perf_counter() - t0
             flops += algorithmic_flops(m, ncols, wl.k)
@@ -407,15 +428,21 @@ def _counter_per_dispatch(path, counter, name_part):
     return float(np.median(list(sums.values()))), len(sums)
 
 
-def write_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+def traffic_path(workload, scales="fp32"):
+    return os.path.join(PROFILES, f"gemm_kernel_{workload}{'_ue8m0' if scales == 'ue8m0' else ''}_traffic.txt")
+
+
+def write_traffic(workload, scales, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     fetch, nf = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", "gemm_kernel")
     write, nw = _counter_per_dispatch(write_csv, "WRITE_SIZE", "gemm_kernel")
     cfetch, _ = _counter_per_dispatch(copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
     cwrite, _ = _counter_per_dispatch(copy_write_csv, "WRITE_SIZE", "copyBuffer")
     fscale, wscale = COPY_BYTES / (cfetch * 1024), COPY_BYTES / (cwrite * 1024)
     traffic = fetch * 1024 * fscale + write * 1024 * wscale
+    sflag = " --scales ue8m0" if scales == "ue8m0" else ""
     lines = [
         f"workload={workload}",
+        f"scales={scales}",
         f"kernel_source_sha256_16={kernel_source_hash()}",
         f"fetch_kib_per_dispatch={fetch:.1f}  (median of {nf} dispatches)",
         f"write_kib_per_dispatch={write:.1f}  (median of {nw} dispatches)",
@@ -427,22 +454,22 @@ def write_traffic(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv
         "  cd /tmp && export TMPDIR=/tmp",
         "  rocprofv3 --pmc FETCH_SIZE -f csv -d $REPO/gpurun_out/pmc_copy_f -o p -- python3 $REPO/bench.py --calibrate-copy",
         "  rocprofv3 --pmc WRITE_SIZE -f csv -d $REPO/gpurun_out/pmc_copy_w -o p -- python3 $REPO/bench.py --calibrate-copy",
-        f"  rocprofv3 --pmc FETCH_SIZE -f csv -d $REPO/gpurun_out/pmc_f -o p -- python3 $REPO/bench.py --launches-only {workload}",
-        f"  rocprofv3 --pmc WRITE_SIZE -f csv -d $REPO/gpurun_out/pmc_w -o p -- python3 $REPO/bench.py --launches-only {workload}",
-        f"  python3 bench.py --launches-only {workload} --write-traffic gpurun_out/pmc_f/p_counter_collection.csv "
+        f"  rocprofv3 --pmc FETCH_SIZE -f csv -d $REPO/gpurun_out/pmc_f -o p -- python3 $REPO/bench.py --launches-only {workload}{sflag}",
+        f"  rocprofv3 --pmc WRITE_SIZE -f csv -d $REPO/gpurun_out/pmc_w -o p -- python3 $REPO/bench.py --launches-only {workload}{sflag}",
+        f"  python3 bench.py --launches-only {workload}{sflag} --write-traffic gpurun_out/pmc_f/p_counter_collection.csv "
         "gpurun_out/pmc_w/p_counter_collection.csv gpurun_out/pmc_copy_f/p_counter_collection.csv "
         "gpurun_out/pmc_copy_w/p_counter_collection.csv",
     ]
-    path = os.path.join(PROFILES, f"gemm_kernel_{workload}_traffic.txt")
+    path = traffic_path(workload, scales)
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(path)
 
 
-def read_traffic(workload):
+def read_traffic(workload, scales="fp32"):
     """Bytes per launch from the committed summary, or None if there is none
     for this workload or the kernel sources changed since it was taken."""
-    path = os.path.join(PROFILES, f"gemm_kernel_{workload}_traffic.txt")
+    path = traffic_path(workload, scales)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -461,7 +488,7 @@ def main(argv=None):
     if args.write_traffic:
         if not args.launches_only:
             raise SystemExit("--write-traffic needs --launches-only WORKLOAD")
-        write_traffic(args.launches_only, *args.write_traffic)
+        write_traffic(args.launches_only, args.scales, *args.write_traffic)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -485,7 +512,7 @@ def main(argv=None):
     if args.launches_only:
         import synth
         wl = {w.name: w for w in synth.workloads() + synth.pages_workloads()}[args.launches_only]
-        p = Prepared(dg, torch, wl)
+        p = Prepared(dg, torch, wl, args.scales)
         for r in range(args.reps):
             p.quant(dg)
             p.gemm(dg, r)
@@ -495,7 +522,7 @@ def main(argv=None):
 
     wls = select_workloads(args.workload)
     headline = [w for w in wls if w.layout == "dense" and w.m == 128] or wls
-    preps = [Prepared(dg, torch, w) for w in headline]
+    preps = [Prepared(dg, torch, w, args.scales) for w in headline]
     torch.cuda.synchronize()
 
     total_ms, gemm_ms = time_steps(dg, torch, preps, args.steps, args.warmup)
@@ -513,7 +540,7 @@ def main(argv=None):
         for w in wls:
             if w in headline:
                 continue
-            p = Prepared(dg, torch, w)
+            p = Prepared(dg, torch, w, args.scales)
             _, g_ms = time_steps(dg, torch, [p], max(5, args.steps // 2), 2)
             extra.append(shape_record(p, float(np.mean(g_ms[:, 0])) * 1e-3, time_quant(dg, torch, p)))
             print(json.dumps(extra[-1]), file=sys.stderr, flush=True)
@@ -531,7 +558,7 @@ def main(argv=None):
     achieved = mean_bytes / mean_dur / 1e9
     # Counter-measured HBM bytes per launch, when every shape of the kernel
     # has a summary taken with the current kernel sources.
-    measured = [read_traffic(preps[i].wl.name) for i in idx]
+    measured = [read_traffic(preps[i].wl.name, args.scales) for i in idx]
     traffic = float(np.mean(measured)) if measured and all(x is not None for x in measured) else None
     roofline = {
         "bound": "hbm",
@@ -540,7 +567,8 @@ def main(argv=None):
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
         "traffic": round(traffic) if traffic is not None else None,
-        "traffic_source": ([f"profiles/gemm_kernel_{preps[i].wl.name}_traffic.txt" for i in idx]
+        "traffic_source": ([os.path.relpath(traffic_path(preps[i].wl.name, args.scales), os.path.dirname(PROFILES))
+                            for i in idx]
                            if traffic is not None else None),
         "kernel": key,
         "launches_averaged": len(idx) * args.steps,
@@ -571,6 +599,7 @@ def main(argv=None):
             "m": headline[0].m,
             "nk_pairs": [[w.n, w.k] for w in headline],
             "step": "dg_quant_1x128(A) + GEMM per shape; weights quantised once before timing",
+            "scales": args.scales,
             "weight_rotation_copies": [len(p.b) for p in preps],
             "num_cus": dg.dg_get_num_cus(),
         },
@@ -579,7 +608,7 @@ def main(argv=None):
         "per_shape": per_shape + extra,
     }
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(headline, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(headline, args.cpu_seconds, args.scales)
     print(json.dumps(result), flush=True)
     return 0
 
