@@ -1022,7 +1022,7 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
     if (c.bm <= 128 && rows <= 128) {
       const int min_slices = c.bm * c.bn >= 128 * 128 ? 16 : 8;
       int parts = std::min(num_cus / std::max(est, 1), nkb / min_slices);
-      if (c.bm * c.bn < 128 * 128) parts = std::min(parts, 4);
+      if (c.bm * c.bn < 128 * 128) parts = std::min(parts, 6);  // 64x2112x7168: 6 parts 3% faster than 4
       if (parts >= 2) sk = parts;
     } else if ((int64_t)est * nkb >= 24LL * num_cus) {
       sk = 1;
