@@ -148,6 +148,39 @@ int dg_grouped_masked_ue8m0(const uint8_t* a, const uint8_t* sfa, const uint8_t*
                             int64_t ld_sfa, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/*
+ * The three fp32-scale GEMMs with a quantised copy of their output, for the
+ * next layer's activations: besides d, every 1x128 tile of the bf16 output
+ * (a row's 128-column block) is quantised exactly as dg_quant_1x128 would
+ * quantise d, in the GEMM's epilogue instead of a second launch.  The pages
+ * leave FP8 casts to the caller and suggest fusing them into the kernel that
+ * produces the activations (project introduction, section Interfaces, the
+ * notice at its start).
+ *   dq  e4m3 [rows][n] (masked: [num_groups][m_max][n]), row stride n
+ *   dsf fp32 [n/128][ld_dsf] (masked: [num_groups][n/128][ld_dsf]), MN-major
+ *       like sfa; ld_dsf >= rows (m, m_total or m_max), a multiple of 4
+ * Rules: n % 128 == 0 (DG_ERR_UNSUPPORTED_SHAPE); dq, dsf 16-byte aligned.
+ * Exactly the rows that d receives are written (padding rows of the
+ * contiguous layout and rows >= masked_m[g] are left untouched in dq and
+ * dsf).  Dense only: the scale padding rows [m, ld_dsf) are written as 0.
+ * The tile shapes used are those whose columns are whole 128-column blocks,
+ * so the configuration (and the workspace need) may differ from the plain
+ * entry point's; dg_get_workspace_size covers both.
+ */
+int dg_fp8_gemm_nt_qout(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                        uint16_t* d, uint8_t* dq, float* dsf, int m, int n, int k, int64_t lda,
+                        int64_t ldb, int64_t ldd, int64_t ld_sfa, int64_t ld_dsf, void* workspace,
+                        size_t workspace_bytes, void* stream);
+int dg_grouped_contiguous_qout(const uint8_t* a, const float* sfa, const uint8_t* b,
+                               const float* sfb, uint16_t* d, uint8_t* dq, float* dsf,
+                               const int32_t* m_indices, int m_total, int n, int k, int num_groups,
+                               int64_t ld_sfa, int64_t ld_dsf, void* workspace,
+                               size_t workspace_bytes, void* stream);
+int dg_grouped_masked_qout(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                           uint16_t* d, uint8_t* dq, float* dsf, const int32_t* masked_m,
+                           int num_groups, int m_max, int n, int k, int expected_m, int64_t ld_sfa,
+                           int64_t ld_dsf, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ----------------------------------------------------------- quantisers -- */
 
 /*
@@ -233,8 +266,9 @@ int64_t dg_get_ue8m0_sfb_leading_dim(int n);
 const char* dg_get_last_error_string(void);
 
 /* Human-readable description of the tile configuration the library would
- * choose for a GEMM (layout 0 = dense, 1 = contiguous, 2 = masked; m is M,
- * M_total or M_max; expected_m is the masked layout's hint, 0 otherwise),
+ * choose for a GEMM (layout 0 = dense, 1 = contiguous, 2 = masked, plus 8 for
+ * the *_qout entry points; m is M, M_total or M_max; expected_m is the masked
+ * layout's hint, 0 otherwise),
  * written into buf (NUL-terminated, truncated to len).  Returns DG_SUCCESS or
  * an error for invalid arguments.  Pure host logic: needs no device. */
 int dg_describe_config(int layout, int m, int n, int k, int num_groups, int expected_m,

@@ -103,9 +103,13 @@ int run_gemm(int layout, dg::GemmParams& p, int rows, int groups, void* ws, size
              void* stream, int expected_m = 0) {
   const int cus = resolve_num_cus();
   if (cus < 0) return fail(DG_ERR_HIP, "cannot query the device's compute-unit count");
-  const dg::GemmConfig cfg = dg::choose_config(layout, rows, p.n, p.k, groups, cus, expected_m);
+  const bool qout = p.dq != nullptr;
+  const dg::GemmConfig cfg = dg::choose_config(layout, rows, p.n, p.k, groups, cus, expected_m, qout);
   if (p.sf_ue8m0 && !dg::ue8m0_variant_built(cfg.variant))
     return fail(DG_ERR_UNSUPPORTED_SHAPE, "tile variant %d is not built for UE8M0 scales", cfg.variant);
+  if (qout && !dg::variant_quantises_output(cfg.variant))
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "tile variant %d cannot quantise its output (columns not whole 128-blocks)",
+                cfg.variant);
   int st = check_workspace(cfg, layout, rows, p.n, groups, ws, ws_bytes);
   if (st != DG_SUCCESS) return st;
   p.workspace = static_cast<float*>(ws);
@@ -117,6 +121,34 @@ int run_gemm(int layout, dg::GemmParams& p, int rows, int groups, void* ws, size
   const hipError_t e = dg::launch_gemm(layout, p, cfg, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_HIP, "GEMM launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+// Optional quantised copy of the output (the *_qout entry points).
+struct QOut {
+  uint8_t* dq;
+  float* dsf;
+  int64_t ld_dsf;
+};
+
+// Checks of the quantised-output arguments; rows = the rows of one group.
+int check_qout(const QOut* q, int rows, int n, int groups) {
+  if (!q) return DG_SUCCESS;
+  if (!q->dq || !q->dsf) return fail(DG_ERR_INVALID_VALUE, "null dq or dsf");
+  if (!aligned16(q->dq) || !aligned16(q->dsf)) return fail(DG_ERR_MISALIGNED, "dq and dsf must be 16-byte aligned");
+  if (n % 128) return fail(DG_ERR_UNSUPPORTED_SHAPE, "n=%d is not a multiple of 128 (quantised output)", n);
+  if (q->ld_dsf < rows || q->ld_dsf < 4) return fail(DG_ERR_INVALID_VALUE, "ld_dsf smaller than the rows or 4");
+  if (q->ld_dsf % 4) return fail(DG_ERR_MISALIGNED, "ld_dsf must be a multiple of 4");
+  if ((int64_t)groups * rows * n >= ((int64_t)1 << 40)) return fail(DG_ERR_UNSUPPORTED_SHAPE, "quantised output too large");
+  return DG_SUCCESS;
+}
+
+void set_qout(dg::GemmParams& p, const QOut* q, int rows, int n) {
+  if (!q) return;
+  p.dq = q->dq;
+  p.dsf = q->dsf;
+  p.ld_dsf = q->ld_dsf;
+  p.dq_gstride = (int64_t)rows * n;
+  p.dsf_gstride = (int64_t)(n / 128) * q->ld_dsf;
 }
 
 // Scale-format fields of GemmParams.  fp32: weight scales [G][ceil(N/128)][K/128].
@@ -131,13 +163,16 @@ void set_scales(dg::GemmParams& p, const void* sfa, const void* sfb, int n, int 
 
 int gemm_nt_impl(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb, uint16_t* d,
                  int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd, int64_t ld_sfa,
-                 void* workspace, size_t workspace_bytes, void* stream, bool ue8m0) {
+                 void* workspace, size_t workspace_bytes, void* stream, bool ue8m0,
+                 const QOut* qo = nullptr) {
   int st = check_gemm_common(a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa);
+  if (st == DG_SUCCESS) st = check_qout(qo, m, n, 1);
   if (st != DG_SUCCESS) return st;
   if (m == 0 || n == 0) return ok();
   dg::GemmParams p{};
   p.a = a; p.b = b; p.d = d;
   set_scales(p, sfa, sfb, n, k, ue8m0);
+  set_qout(p, qo, m, n);
   p.m = m; p.n = n; p.k = k; p.num_groups = 1;
   p.lda = lda; p.ldb = ldb; p.ldd = ldd; p.ld_sfa = ld_sfa;
   return run_gemm(dg::kDense, p, m, 1, workspace, workspace_bytes, stream);
@@ -145,9 +180,11 @@ int gemm_nt_impl(const uint8_t* a, const void* sfa, const uint8_t* b, const void
 
 int contiguous_impl(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb, uint16_t* d,
                     const int32_t* m_indices, int m_total, int n, int k, int num_groups, int64_t ld_sfa,
-                    void* workspace, size_t workspace_bytes, void* stream, bool ue8m0) {
+                    void* workspace, size_t workspace_bytes, void* stream, bool ue8m0,
+                    const QOut* qo = nullptr) {
   if (num_groups < 1) return fail(DG_ERR_INVALID_VALUE, "num_groups must be >= 1");
   int st = check_gemm_common(a, sfa, b, sfb, d, m_total, n, k, k, k, n, ld_sfa);
+  if (st == DG_SUCCESS) st = check_qout(qo, m_total, n, 1);
   if (st != DG_SUCCESS) return st;
   if (!m_indices) return fail(DG_ERR_INVALID_VALUE, "null m_indices");
   if (m_total % 128) return fail(DG_ERR_UNSUPPORTED_SHAPE, "m_total=%d is not a multiple of 128", m_total);
@@ -156,6 +193,7 @@ int contiguous_impl(const uint8_t* a, const void* sfa, const uint8_t* b, const v
   dg::GemmParams p{};
   p.a = a; p.b = b; p.d = d; p.m_indices = m_indices;
   set_scales(p, sfa, sfb, n, k, ue8m0);
+  set_qout(p, qo, m_total, n);
   p.m = m_total; p.n = n; p.k = k; p.num_groups = num_groups;
   p.lda = k; p.ldb = k; p.ldd = n; p.ld_sfa = ld_sfa;
   p.b_gstride = (int64_t)n * k;
@@ -164,10 +202,12 @@ int contiguous_impl(const uint8_t* a, const void* sfa, const uint8_t* b, const v
 
 int masked_impl(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb, uint16_t* d,
                 const int32_t* masked_m, int num_groups, int m_max, int n, int k, int expected_m,
-                int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream, bool ue8m0) {
+                int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream, bool ue8m0,
+                const QOut* qo = nullptr) {
   if (num_groups < 1) return fail(DG_ERR_INVALID_VALUE, "num_groups must be >= 1");
   if (expected_m < 0) return fail(DG_ERR_INVALID_VALUE, "expected_m must be >= 0");
   int st = check_gemm_common(a, sfa, b, sfb, d, m_max, n, k, k, k, n, ld_sfa);
+  if (st == DG_SUCCESS) st = check_qout(qo, m_max, n, num_groups);
   if (st != DG_SUCCESS) return st;
   if (!masked_m) return fail(DG_ERR_INVALID_VALUE, "null masked_m");
   if (n % 8) return fail(DG_ERR_MISALIGNED, "n must be a multiple of 8 (rows of d are packed)");
@@ -176,6 +216,7 @@ int masked_impl(const uint8_t* a, const void* sfa, const uint8_t* b, const void*
   dg::GemmParams p{};
   p.a = a; p.b = b; p.d = d; p.masked_m = masked_m;
   set_scales(p, sfa, sfb, n, k, ue8m0);
+  set_qout(p, qo, m_max, n);
   p.m = m_max; p.n = n; p.k = k; p.num_groups = num_groups;
   p.lda = k; p.ldb = k; p.ldd = n; p.ld_sfa = ld_sfa;
   p.a_gstride = (int64_t)m_max * k;
@@ -267,6 +308,34 @@ int dg_grouped_masked_ue8m0(const uint8_t* a, const uint8_t* sfa, const uint8_t*
                      workspace, workspace_bytes, stream, true);
 }
 
+int dg_fp8_gemm_nt_qout(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                        uint16_t* d, uint8_t* dq, float* dsf, int m, int n, int k, int64_t lda,
+                        int64_t ldb, int64_t ldd, int64_t ld_sfa, int64_t ld_dsf, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const QOut q{dq, dsf, ld_dsf};
+  return gemm_nt_impl(a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, workspace, workspace_bytes,
+                      stream, false, &q);
+}
+
+int dg_grouped_contiguous_qout(const uint8_t* a, const float* sfa, const uint8_t* b,
+                               const float* sfb, uint16_t* d, uint8_t* dq, float* dsf,
+                               const int32_t* m_indices, int m_total, int n, int k, int num_groups,
+                               int64_t ld_sfa, int64_t ld_dsf, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  const QOut q{dq, dsf, ld_dsf};
+  return contiguous_impl(a, sfa, b, sfb, d, m_indices, m_total, n, k, num_groups, ld_sfa, workspace,
+                         workspace_bytes, stream, false, &q);
+}
+
+int dg_grouped_masked_qout(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                           uint16_t* d, uint8_t* dq, float* dsf, const int32_t* masked_m,
+                           int num_groups, int m_max, int n, int k, int expected_m, int64_t ld_sfa,
+                           int64_t ld_dsf, void* workspace, size_t workspace_bytes, void* stream) {
+  const QOut q{dq, dsf, ld_dsf};
+  return masked_impl(a, sfa, b, sfb, d, masked_m, num_groups, m_max, n, k, expected_m, ld_sfa,
+                     workspace, workspace_bytes, stream, false, &q);
+}
+
 int dg_quant_1x128(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
                    int64_t ld_sf, int num_groups, void* stream) {
   return quant_1x128_impl(x, q, sf, rows, cols, ld_sf, num_groups, false, stream);
@@ -296,17 +365,19 @@ size_t dg_get_workspace_size(int m, int n, int k, int num_groups) {
   if (m <= 0 || n <= 0 || k <= 0 || num_groups < 1) return 0;
   int cus = resolve_num_cus();
   if (cus < 0) cus = 256;
-  // The largest need over the layouts and, for the masked layout, over the
-  // tile shapes its expected_m hint can select.
+  // The largest need over the layouts, with and without a quantised output,
+  // and, for the masked layout, over the tile shapes its expected_m hint can
+  // select.
   size_t worst = 0;
   const int hints[] = {0, 1, 64, 65, 128, 129, 256, 257};
-  for (int layout = dg::kDense; layout <= dg::kMasked; ++layout)
-    for (int h : hints) {
-      if (h && layout != dg::kMasked) break;
-      const dg::GemmConfig c = dg::choose_config(layout, m, n, k, num_groups, cus, h);
-      const size_t need = dg::workspace_bytes_for(c, layout, m, n, num_groups);
-      if (need > worst) worst = need;
-    }
+  for (int qout = 0; qout <= 1; ++qout)
+    for (int layout = dg::kDense; layout <= dg::kMasked; ++layout)
+      for (int h : hints) {
+        if (h && layout != dg::kMasked) break;
+        const dg::GemmConfig c = dg::choose_config(layout, m, n, k, num_groups, cus, h, qout != 0);
+        const size_t need = dg::workspace_bytes_for(c, layout, m, n, num_groups);
+        if (need > worst) worst = need;
+      }
   return worst;
 }
 
@@ -333,10 +404,12 @@ const char* dg_get_last_error_string(void) { return g_last_error; }
 
 int dg_describe_config(int layout, int m, int n, int k, int num_groups, int expected_m,
                        int num_cus, char* buf, size_t len) {
+  const bool qout = (layout & 8) != 0;  // configuration of the *_qout entry points
+  layout &= ~8;
   if (layout < dg::kDense || layout > dg::kMasked || m < 0 || n < 0 || k < 0 ||
       num_groups < 1 || expected_m < 0 || num_cus < 1 || !buf || len == 0)
     return fail(DG_ERR_INVALID_VALUE, "bad arguments to dg_describe_config");
-  const dg::GemmConfig c = dg::choose_config(layout, m, n, k, num_groups, num_cus, expected_m);
+  const dg::GemmConfig c = dg::choose_config(layout, m, n, k, num_groups, num_cus, expected_m, qout);
   snprintf(buf, len, "layout=%s bm=%d bn=%d stream_k=%d sk_split=%d grid=%d tiles=%d variant=%d k_rotate=%d workspace=%zu",
            layout_name(layout), c.bm, c.bn, c.stream_k, c.sk_split, c.grid, c.tiles, c.variant, c.k_rotate,
            dg::workspace_bytes_for(c, layout, m, n, num_groups));

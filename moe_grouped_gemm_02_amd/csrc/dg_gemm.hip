@@ -311,11 +311,17 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
     const uint8_t* A = p.a;
     const float* SA = p.sfa;
     uint16_t* D = p.d;
+    uint8_t* DQ = p.dq;
+    float* DSF = p.dsf;
     if (LAYOUT == kMasked) {
       rows_valid = clamp_rows(p.masked_m[g], p.m);
       A += (int64_t)g * p.a_gstride;
       SA = scale_ptr<SF>(SA, (int64_t)g * p.sfa_gstride);
       D += (int64_t)g * p.d_gstride;
+      if (DQ) {
+        DQ += (int64_t)g * p.dq_gstride;
+        DSF += (int64_t)g * p.dsf_gstride;
+      }
     }
     // Contiguous layout: the experts of the tile's 128-row halves.  A tile
     // whose halves belong to two experts is computed once per expert.
@@ -844,6 +850,25 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
       static_assert(kER * kRowBytes <= T::STAGES * T::kStageBytes, "epilogue tile does not fit");
       static_assert(kER == T::BM || kER == T::TM, "epilogue pass must be whole wave rows");
       const bool odd = fr & 1;
+      // Round and pair up first: the packed words take half the registers
+      // of the fp32 accumulators, which are dead from here on.
+      uint32_t packed[T::FM][T::FN][2];
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::FN; ++j) {
+          const uint32_t b0 = f32_to_bf16_rne(acc[i][j][0]), b1 = f32_to_bf16_rne(acc[i][j][1]);
+          const uint32_t b2 = f32_to_bf16_rne(acc[i][j][2]), b3 = f32_to_bf16_rne(acc[i][j][3]);
+          const uint32_t send = odd ? (b0 | (b1 << 16)) : (b2 | (b3 << 16));
+          const uint32_t recv = (uint32_t)__shfl_xor((int)send, 1, 64);
+          if (odd) {  // rows 4kg+2, 4kg+3; columns fr-1, fr
+            packed[i][j][0] = (recv & 0xFFFFu) | (b2 << 16);
+            packed[i][j][1] = (recv >> 16) | (b3 << 16);
+          } else {    // rows 4kg+0, 4kg+1; columns fr, fr+1
+            packed[i][j][0] = b0 | ((recv & 0xFFFFu) << 16);
+            packed[i][j][1] = b1 | ((recv >> 16) << 16);
+          }
+        }
 #pragma unroll
       for (int er = 0; er < T::BM / kER; ++er) {
         lds_barrier();  // LDS free: the K loop (or previous pass) is done reading
@@ -853,23 +878,11 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
           for (int i = 0; i < T::FM; ++i)
 #pragma unroll
             for (int j = 0; j < T::FN; ++j) {
-              const uint32_t b0 = f32_to_bf16_rne(acc[i][j][0]), b1 = f32_to_bf16_rne(acc[i][j][1]);
-              const uint32_t b2 = f32_to_bf16_rne(acc[i][j][2]), b3 = f32_to_bf16_rne(acc[i][j][3]);
-              const uint32_t send = odd ? (b0 | (b1 << 16)) : (b2 | (b3 << 16));
-              const uint32_t recv = (uint32_t)__shfl_xor((int)send, 1, 64);
-              uint32_t w0, w1;
-              if (odd) {  // rows 4kg+2, 4kg+3; columns fr-1, fr
-                w0 = (recv & 0xFFFFu) | (b2 << 16);
-                w1 = (recv >> 16) | (b3 << 16);
-              } else {    // rows 4kg+0, 4kg+1; columns fr, fr+1
-                w0 = b0 | ((recv & 0xFFFFu) << 16);
-                w1 = b1 | ((recv >> 16) << 16);
-              }
               const int r = rbase + i * 16 + 4 * kg + (odd ? 2 : 0);
               const int c = wn * T::TN + j * 16 + (fr & ~1);
               uint8_t* dst = smem + r * kRowBytes + c * 2;
-              *reinterpret_cast<uint32_t*>(dst) = w0;
-              *reinterpret_cast<uint32_t*>(dst + kRowBytes) = w1;
+              *reinterpret_cast<uint32_t*>(dst) = packed[i][j][0];
+              *reinterpret_cast<uint32_t*>(dst + kRowBytes) = packed[i][j][1];
             }
         }
         lds_barrier();
@@ -889,6 +902,56 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
           } else {
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
             for (int e = 0; e < p.n - col; ++e) drow[col + e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+          }
+        }
+        if constexpr (T::BN % 128 == 0) {
+          if (DQ) {
+            // Quantised copy of the output rows just staged: every 1x128 tile
+            // (a row's 128-column block; the tile's columns are whole blocks)
+            // gets s = amax/448 and e4m3(x/s) computed from the bf16 values,
+            // as the activation quantiser computes them.  Eight consecutive
+            // lanes own one block of a row, 16 values each; every lane runs
+            // every iteration so the amax shuffles see all eight.
+            constexpr int kQPerRow = T::BN / 16;
+            static_assert((kER * kQPerRow) % T::kThreads == 0, "uneven quantisation passes");
+            for (int idx = tid; idx < kER * kQPerRow; idx += T::kThreads) {
+              const int rl = idx / kQPerRow, qc = idx - rl * kQPerRow;
+              const int row = m0 + er * kER + rl;
+              const int col = n0 + qc * 16;
+              bool ok = row < rows_valid && row < m0 + T::BM && col < p.n;
+              if (LAYOUT == kContiguous && ok) ok = p.m_indices[row] == g;
+              const uint4 lo = *reinterpret_cast<const uint4*>(smem + rl * kRowBytes + qc * 32);
+              const uint4 hi = *reinterpret_cast<const uint4*>(smem + rl * kRowBytes + qc * 32 + 16);
+              const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+              float amax = 0.0f;
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w[e] & 0xFFFFu)), fabsf(bf16_bits_to_f32(w[e] >> 16))));
+#pragma unroll
+              for (int off = 4; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 8));
+              const float s_out = amax / 448.0f;
+              const double rcp = tile_reciprocal(s_out);
+              uint32_t out[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                out[e] = e4m3_x4(quotient(w[2 * e] & 0xFFFFu, rcp), quotient(w[2 * e] >> 16, rcp),
+                                 quotient(w[2 * e + 1] & 0xFFFFu, rcp), quotient(w[2 * e + 1] >> 16, rcp));
+              if (ok) {
+                *reinterpret_cast<uint4*>(DQ + (int64_t)row * p.n + col) = make_uint4(out[0], out[1], out[2], out[3]);
+                if ((qc & 7) == 0) DSF[(int64_t)(col >> 7) * p.ld_dsf + row] = s_out;
+              }
+            }
+          }
+        }
+      }
+      if constexpr (T::BN % 128 == 0) {
+        // Dense layout: the tile holding the last rows also zeroes the scale
+        // padding rows [M, ld_dsf) of its column blocks, as the quantiser does.
+        if (DQ && LAYOUT == kDense && m0 + T::BM >= p.m) {
+          const int pad = (int)(p.ld_dsf - p.m);
+          for (int idx = tid; idx < pad * (T::BN / 128); idx += T::kThreads) {
+            const int cb = (n0 >> 7) + idx / pad;
+            if (cb * 128 < p.n) DSF[(int64_t)cb * p.ld_dsf + p.m + idx % pad] = 0.0f;
           }
         }
       }
@@ -983,7 +1046,11 @@ int forced_rotate() {  // third field: 0 or 1, -1 when absent
 
 }  // namespace
 
-GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cus, int expected_m) {
+bool variant_quantises_output(int variant) {
+  return variant >= 0 && variant < kNumVariants && kVariants[variant].bn % 128 == 0;
+}
+
+GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cus, int expected_m, bool qout) {
   // m: dense M, contiguous M_total, masked M_max.  The rules below come from
   // sweeps over tile variants on the benchmark shapes.  For the masked
   // layout a host hint of the typical valid rows per group replaces M_max in
@@ -1003,6 +1070,10 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
   } else {
     v = tiles_of(256, 256) >= num_cus / 2 ? 0 : 1;
   }
+  // A quantised output needs whole 128-column blocks per tile: the 64-wide
+  // decode tiles give way to the 128x128 one.
+  const bool widened = qout && kVariants[v].bn % 128 != 0;
+  if (widened) v = 6;
   const int fv = forced_variant();
   if (fv >= 0 && fv < kNumVariants) v = fv;
   GemmConfig c{};
@@ -1020,7 +1091,10 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
   int sk = 0;  // 0: data-parallel, 1: equal runs, S >= 2: S parts per tile
   if (layout != kContiguous && nkb >= 2 && 10 * est < 7 * num_cus) {
     if (c.bm <= 128 && rows <= 128) {
-      const int min_slices = c.bm * c.bn >= 128 * 128 ? 16 : 8;
+      // Shorter parts for the 128x128 tiles that stand in for 64-wide ones
+      // (quantised output): fewer tiles, so more parts (64x4096x7168 fused:
+      // 27.5 -> 24.2 us with 8 parts instead of 3).
+      const int min_slices = (c.bm * c.bn >= 128 * 128 && !widened) ? 16 : 8;
       int parts = std::min(num_cus / std::max(est, 1), nkb / min_slices);
       if (c.bm * c.bn < 128 * 128) parts = std::min(parts, 6);  // 64x2112x7168: 6 parts 3% faster than 4
       if (parts >= 2) sk = parts;

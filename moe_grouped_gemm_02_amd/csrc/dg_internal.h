@@ -30,6 +30,12 @@ struct GemmParams {
   // strides count bytes.
   int sf_ue8m0;
   int64_t ld_sfb;
+  // Quantised copy of the output (null: none): e4m3 codes [G][rows][n] and
+  // fp32 scales [G][n/128][ld_dsf] of every 1x128 tile of D, as the
+  // activation quantiser would compute them from the bf16 output.
+  uint8_t* dq;
+  float* dsf;
+  int64_t ld_dsf, dq_gstride, dsf_gstride;
 };
 
 // Tile variants built with UE8M0 scales.
@@ -63,7 +69,12 @@ struct Schedule {
 
 // expected_m (masked layout only, 0 = unknown): typical valid rows per group,
 // used to pick the tile shape.
-GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cus, int expected_m = 0);
+// qout: the call also quantises its output, which needs tiles whose columns
+// are whole 128-column blocks.
+GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cus, int expected_m = 0,
+                         bool qout = false);
+// Whether a tile variant's columns are whole 128-column blocks.
+bool variant_quantises_output(int variant);
 size_t workspace_bytes_for(const GemmConfig& cfg, int layout, int m, int n, int groups);
 
 hipError_t launch_gemm(int layout, const GemmParams& p, const GemmConfig& cfg,

@@ -14,34 +14,6 @@
 
 namespace dg {
 
-// Division and encoding, shared by both quantisers.
-//
-// q = fp32(x / s) is formed as fp32((double)x * RN64(1 / (double)s)): one
-// correctly rounded fp64 reciprocal per tile, then one fp64 multiply per
-// element.  For a bf16 x (8 significant bits) and an fp32 s (24 bits) the
-// exact quotient lies at least 2^-49 (relative) away from any fp32 rounding
-// boundary, while this product is within about 2^-52 of it, so rounding it
-// to fp32 gives the IEEE quotient itself (also checked exhaustively on the
-// host: every s = fp32(a / 448) over the positive finite bf16 a, against every
-// bf16 x with |x| <= a, 1.07e9 pairs, no difference).  A zero tile (s = 0)
-// uses a zero reciprocal, which keeps each x's signed zero.
-__device__ __forceinline__ double tile_reciprocal(float s) { return s == 0.0f ? 0.0 : 1.0 / (double)s; }
-
-__device__ __forceinline__ float quotient(uint32_t bf16_bits, double rcp) {
-  return (float)((double)bf16_bits_to_f32(bf16_bits) * rcp);
-}
-
-// e4m3 codes of four quotients, packed little-endian into one word, by the
-// hardware fp32 -> fp8 conversion (OCP e4m3fn, round to nearest even, signed
-// zero kept).  It agrees with the encoding rule of f32_to_e4m3_rne for every
-// fp32 value of magnitude below 450 (checked on gfx950 for all 2.28e9 such bit
-// patterns); quotients here are at most 448 * (1 + 2^-24).
-__device__ __forceinline__ uint32_t e4m3_x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return (uint32_t)w;
-}
-
 // Power-of-two (UE8M0) scales: E = ceil(log2(amax / 448)) + 127, clamped to
 // [0, 254], 0 for an all-zero tile; the scale is 2^(E - 127).  The quotient
 // amax/448 is formed in fp64: for a bf16 amax it is either exactly a power of

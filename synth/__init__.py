@@ -34,6 +34,23 @@ def bf16_normal(shape, seed: int, scale: float = 1.0) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
+# bf16 patterns of 0, +-0.5, +-1 and +-1.75.
+_GRID_BITS = np.array([0x0000, 0x3F00, 0xBF00, 0x3F80, 0xBF80, 0x3FE0, 0xBFE0], dtype=np.uint16)
+
+
+def bf16_grid(shape, seed: int) -> np.ndarray:
+    """Values drawn uniformly from {0, +-0.5, +-1, +-1.75}, with +1.75 placed at
+    the first element of every 128-wide slice of the last axis, as uint16 bf16
+    patterns.  Every 1x128 tile (and so every 128x128 block) then has amax
+    1.75, a value set on which products and sums stay small dyadic numbers."""
+    if shape[-1] % 128:
+        raise ValueError("last axis must be a multiple of 128")
+    rng = np.random.default_rng(seed)
+    x = _GRID_BITS[rng.integers(0, _GRID_BITS.size, size=shape)]
+    x[..., ::128] = 0x3FE0
+    return x
+
+
 def contiguous_m_indices(segment_rows, pad_rows=None, order=None) -> np.ndarray:
     """Per-row expert ids for the contiguous layout.
 

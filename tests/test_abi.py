@@ -132,3 +132,40 @@ def test_describe_config_is_host_only():
     assert "bm=" in s and "bn=" in s and "stream_k=" in s
     with pytest.raises(dg.DGError):
         dg.dg_describe_config(7, 1, 1, 128)
+
+
+def _gemm_qout(**kw):
+    args = dict(a=FAKE, sfa=FAKE, b=FAKE, sfb=FAKE, d=FAKE, dq=FAKE, dsf=FAKE, m=64, n=2048, k=7168,
+                lda=7168, ldb=7168, ldd=2048, ld_sfa=64, ld_dsf=64, ws=None, ws_bytes=0, stream=None)
+    args.update(kw)
+    ptrs = ("a", "sfa", "b", "sfb", "d", "dq", "dsf", "ws", "stream")
+    order = ("a", "sfa", "b", "sfb", "d", "dq", "dsf", "m", "n", "k", "lda", "ldb", "ldd", "ld_sfa", "ld_dsf",
+             "ws", "ws_bytes", "stream")
+    return dg.raw().dg_fp8_gemm_nt_qout(*[ctypes.c_void_p(args[x]) if x in ptrs else args[x] for x in order])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=2112, ldd=2112), -2),   # a 1x128 output tile would be cut
+    (dict(dq=0), -1),
+    (dict(dsf=0), -1),
+    (dict(dq=FAKE + 4), -3),
+    (dict(ld_dsf=60), -1),
+    (dict(ld_dsf=66), -3),
+    (dict(ld_sfa=60), -1),          # the plain checks still apply
+])
+def test_qout_argument_errors(kw, status):
+    assert _gemm_qout(**kw) == status
+    assert dg.dg_get_last_error_string() != ""
+
+
+def test_qout_configuration_uses_whole_column_blocks():
+    # M = 64 decode shapes pick 64x64 tiles; the quantised-output form takes
+    # 128-column tiles instead, and the workspace query covers both.
+    plain = dict(kv.split("=") for kv in dg.dg_describe_config(0, 64, 2048, 7168, 1, 256).split())
+    fused = dict(kv.split("=") for kv in dg.dg_describe_config(8, 64, 2048, 7168, 1, 256).split())
+    assert int(plain["bn"]) == 64 and int(fused["bn"]) % 128 == 0
+    dg.dg_set_num_cus(256)
+    try:
+        assert dg.dg_get_workspace_size(64, 2048, 7168, 1) >= max(int(plain["workspace"]), int(fused["workspace"]))
+    finally:
+        dg.dg_set_num_cus(0)

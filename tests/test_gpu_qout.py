@@ -1,0 +1,204 @@
+"""GPU parity of the GEMMs that also quantise their output (the *_qout entry
+points), against the oracle's GEMM followed by the oracle's 1x128 quantiser.
+
+Exact inputs (synth.bf16_grid): A and B take values in {0, +-0.5, +-1, +-1.75}
+with 1.75 in every 1x128 tile, so every scale is 2^-8 and every code one of
+0, +-128, +-256, +-448 (all multiples of 2^6): each slice's partial product
+is a multiple of 2^12 below 2^25 and each promoted term a multiple of 2^-4,
+so the fp32 result is exact whatever the summation order (the fixture checks
+the multiple-of-2^-4 property of the oracle's result).  The GPU's bf16 output must then equal the oracle's RNE
+rounding of its fp64 result bit for bit, and the quantised output must equal
+the oracle quantiser applied to that bf16 matrix bit for bit (codes, scales
+and the zeroed scale padding of the dense layout).  This runs for every tile
+variant whose columns are whole 128-column blocks, with every work division,
+and for the three layouts; rows a layout does not write keep their sentinel
+in d, dq and dsf.
+
+Random N(0,1) inputs: d meets the bf16 tolerance rule; every 1x128 output
+tile whose bf16 values equal the oracle's rounding has codes and scale equal
+to the oracle's quantisation; on the remaining tiles the dequantised output
+stays within the GEMM tolerance plus one e4m3 rounding of the oracle's
+result.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import bf16, e4m3, gemm, quant
+from tests.gpu_util import SENTINEL, bf16_to_f64, dev, host, require_gpu
+from tests.tolerance import check
+
+pytestmark = pytest.mark.gpu
+
+QOUT_VARIANTS = [0, 1, 3, 5, 6, 8, 9, 10]  # columns are whole 128-column blocks
+M, N, K = 150, 384, 1536
+Q_SENT = 0x5A
+SF_SENT = -3.25
+
+
+def _ws(dg, m, n, k, groups=1):
+    size = dg.dg_get_workspace_size(m, n, k, groups)
+    return torch.zeros(size, dtype=torch.uint8, device="cuda") if size else None
+
+
+def _outputs(shape, n, ld):
+    d = torch.full(shape + (n,), SENTINEL, dtype=torch.int16, device="cuda")
+    dq = torch.full(shape + (n,), Q_SENT, dtype=torch.uint8, device="cuda")
+    dsf_shape = ((shape[0],) if len(shape) == 2 else ()) + (n // 128, ld)
+    dsf = torch.full(dsf_shape, SF_SENT, dtype=torch.float32, device="cuda")
+    return d, dq, dsf
+
+
+def _same_f32(a, b):
+    return np.array_equal(np.asarray(a, np.float32).view(np.uint32), np.asarray(b, np.float32).view(np.uint32))
+
+
+@pytest.fixture
+def force(monkeypatch):
+    def _set(variant, division, rotate=0):
+        monkeypatch.setenv("DG_FORCE_CONFIG", f"{variant}:{division}:{rotate}")
+    yield _set
+    monkeypatch.delenv("DG_FORCE_CONFIG", raising=False)
+
+
+@pytest.fixture(scope="module")
+def exact_dense():
+    a, sfa = quant.quant_1x128(synth.bf16_grid((M, K), 801))
+    b, sfb = quant.quant_128x128(synth.bf16_grid((N, K), 802))
+    assert np.all(sfa[:, :M] == 2.0 ** -8) and np.all(sfb == 2.0 ** -8)
+    d64 = gemm.gemm_nt_ref(a, sfa, b, sfb)
+    assert np.all(d64 * 16 == np.round(d64 * 16)) and np.abs(d64).max() < 2.0 ** 19
+    d_bits = bf16.bits_from_f64(d64)
+    ld = quant.sf_leading_dim(M) + 4  # a padded scale matrix: rows [M, ld) must come back as 0
+    q_ref, sf_ref = quant.quant_1x128(d_bits, ld_sf=ld)
+    return a, sfa, b, sfb, d_bits, q_ref, sf_ref, ld
+
+
+def _run_exact_dense(dg, ops, what):
+    a, sfa, b, sfb, d_bits, q_ref, sf_ref, ld = ops
+    d, dq, dsf = _outputs((M,), N, ld)
+    dg.dg_fp8_gemm_nt_qout(dev(a), dev(sfa), dev(b), dev(sfb), d, dq, dsf, workspace=_ws(dg, M, N, K))
+    assert np.array_equal(host(d), d_bits), f"{what}: bf16 output differs from the exact result"
+    assert np.array_equal(host(dq), q_ref), f"{what}: codes differ"
+    assert _same_f32(host(dsf), sf_ref), f"{what}: scales differ"
+
+
+def test_exact_dense_default(exact_dense):
+    _run_exact_dense(require_gpu(), exact_dense, "default")
+
+
+@pytest.mark.parametrize("division", [0, 1, 3])
+@pytest.mark.parametrize("variant", QOUT_VARIANTS)
+def test_exact_dense_every_variant(variant, division, force, exact_dense):
+    dg = require_gpu()
+    force(variant, division)
+    _run_exact_dense(dg, exact_dense, f"variant {variant} division {division}")
+
+
+def test_narrow_tile_is_rejected(force, exact_dense):
+    dg = require_gpu()
+    force(4, 0)  # 64-column tiles cannot quantise whole 128-column blocks
+    a, sfa, b, sfb, _, _, _, ld = exact_dense
+    d, dq, dsf = _outputs((M,), N, ld)
+    with pytest.raises(dg.DGError) as err:
+        dg.dg_fp8_gemm_nt_qout(dev(a), dev(sfa), dev(b), dev(sfb), d, dq, dsf, workspace=_ws(dg, M, N, K))
+    assert err.value.status == -2
+    torch.cuda.synchronize()
+    assert bool((dq == Q_SENT).all())
+
+
+def test_decode_shape_default_config():
+    """M = 64 picks 64-column tiles for the plain GEMM; the fused form must
+    still give the exact answer with its own tile choice."""
+    dg = require_gpu()
+    m, n, k = 64, 2048, 7168
+    a, sfa = quant.quant_1x128(synth.bf16_grid((m, k), 811))
+    b, sfb = quant.quant_128x128(synth.bf16_grid((n, k), 812))
+    d_bits = bf16.bits_from_f64(gemm.gemm_nt_ref(a, sfa, b, sfb))
+    q_ref, sf_ref = quant.quant_1x128(d_bits)
+    d, dq, dsf = _outputs((m,), n, quant.sf_leading_dim(m))
+    dg.dg_fp8_gemm_nt_qout(dev(a), dev(sfa), dev(b), dev(sfb), d, dq, dsf, workspace=_ws(dg, m, n, k))
+    assert np.array_equal(host(d), d_bits)
+    assert np.array_equal(host(dq), q_ref)
+    assert _same_f32(host(dsf), sf_ref)
+
+
+@pytest.mark.parametrize("division", [0, 1, 3])
+@pytest.mark.parametrize("variant", [0, 1, 6, 9])
+def test_exact_masked(variant, division, force):
+    dg = require_gpu()
+    force(variant, division)
+    g, m_max = 3, 160
+    mm = np.array([150, 0, 77], dtype=np.int32)
+    a, sfa = quant.quant_1x128(synth.bf16_grid((g, m_max, K), 821))
+    b, sfb = quant.quant_128x128(synth.bf16_grid((g, N, K), 822))
+    ref, written = gemm.grouped_masked_ref(a, sfa, b, sfb, mm)
+    d_bits = bf16.bits_from_f64(np.where(written[..., None] if written.ndim == 2 else written, ref, 0.0))
+    q_ref, sf_ref = quant.quant_1x128(d_bits)
+    ld = sf_ref.shape[-1]
+    d, dq, dsf = _outputs((g, m_max), N, ld)
+    dg.dg_grouped_masked_qout(dev(a), dev(sfa), dev(b), dev(sfb), d, dq, dsf, dev(mm), expected_m=int(mm.mean()),
+                              workspace=_ws(dg, m_max, N, K, g))
+    d_h, q_h, sf_h = host(d), host(dq), host(dsf)
+    for grp in range(g):
+        v = int(mm[grp])
+        assert np.array_equal(d_h[grp, :v], d_bits[grp, :v]), f"group {grp}: bf16 output"
+        assert np.all(d_h[grp, v:] == SENTINEL), f"group {grp}: rows past masked_m written"
+        assert np.array_equal(q_h[grp, :v], q_ref[grp, :v]), f"group {grp}: codes"
+        assert np.all(q_h[grp, v:] == Q_SENT), f"group {grp}: codes past masked_m written"
+        assert _same_f32(sf_h[grp][:, :v], sf_ref[grp][:, :v]), f"group {grp}: scales"
+        assert np.all(sf_h[grp][:, v:] == np.float32(SF_SENT)), f"group {grp}: scales past masked_m written"
+
+
+@pytest.mark.parametrize("variant", [0, 1, 6])
+def test_exact_contiguous(variant, force):
+    dg = require_gpu()
+    force(variant, 0)
+    g = 3
+    mi = synth.contiguous_m_indices([128, 384, 256], [0, 128, 0], [2, 0, 1])
+    m_total = mi.size
+    a, sfa = quant.quant_1x128(synth.bf16_grid((m_total, K), 831))
+    b, sfb = quant.quant_128x128(synth.bf16_grid((g, N, K), 832))
+    ref, written = gemm.grouped_contiguous_ref(a, sfa, b, sfb, mi)
+    rows = np.flatnonzero(mi >= 0)
+    d_bits = bf16.bits_from_f64(ref[rows])
+    q_ref, sf_ref = quant.quant_1x128(d_bits)
+    d, dq, dsf = _outputs((m_total,), N, m_total)
+    dg.dg_grouped_contiguous_qout(dev(a), dev(sfa), dev(b), dev(sfb), d, dq, dsf, dev(mi.astype(np.int32)),
+                                  workspace=_ws(dg, m_total, N, K, g))
+    d_h, q_h, sf_h = host(d), host(dq), host(dsf)
+    pad = np.flatnonzero(mi < 0)
+    assert np.array_equal(d_h[rows], d_bits)
+    assert np.array_equal(q_h[rows], q_ref)
+    assert _same_f32(sf_h[:, rows], sf_ref[:, :rows.size])
+    assert np.all(d_h[pad] == SENTINEL) and np.all(q_h[pad] == Q_SENT)
+    assert np.all(sf_h[:, pad] == np.float32(SF_SENT))
+
+
+@pytest.mark.parametrize("m,n,k", [(128, 2048, 7168), (150, 1024, 1536), (4096, 512, 1024)])
+def test_random_inputs(m, n, k):
+    dg = require_gpu()
+    a, sfa = quant.quant_1x128(synth.bf16_normal((m, k), 841 + m))
+    b, sfb = quant.quant_128x128(synth.bf16_normal((n, k), 842 + n))
+    d64 = gemm.gemm_nt_ref(a, sfa, b, sfb)
+    d_bits = bf16.bits_from_f64(d64)
+    q_ref, sf_ref = quant.quant_1x128(d_bits)
+    d, dq, dsf = _outputs((m,), n, quant.sf_leading_dim(m))
+    dg.dg_fp8_gemm_nt_qout(dev(a), dev(sfa), dev(b), dev(sfb), d, dq, dsf, workspace=_ws(dg, m, n, k))
+    d_h, q_h, sf_h = host(d), host(dq), host(dsf)
+    check(bf16_to_f64(d_h), d64, f"random {m}x{n}x{k}")
+    # Tiles whose bf16 values agree exactly with the oracle's rounding.
+    same = (d_h == d_bits).reshape(m, n // 128, 128).all(axis=2)  # [m][n/128]
+    assert same.sum() >= 100, "too few tiles agree exactly to be a test"
+    q3, qr3 = q_h.reshape(m, n // 128, 128), q_ref.reshape(m, n // 128, 128)
+    assert np.array_equal(q3[same], qr3[same])
+    assert _same_f32(sf_h[:, :m].T[same], sf_ref[:, :m].T[same])
+    assert np.all(sf_h[:, m:] == 0)
+    # Every tile: dequantised output near the oracle's result.
+    deq = e4m3.decode(q_h).reshape(m, n // 128, 128) * sf_h[:, :m].T[:, :, None].astype(np.float64)
+    ref = d64.reshape(m, n // 128, 128)
+    rms = np.sqrt(np.mean(d64 ** 2))
+    bound = 1e-2 * rms + (2.0 ** -8 + 2.0 ** -4) * np.abs(ref) + 2.0 ** -9 * sf_h[:, :m].T[:, :, None]
+    assert np.all(np.abs(deq - ref) <= bound)
