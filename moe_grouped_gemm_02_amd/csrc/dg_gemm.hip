@@ -1097,6 +1097,9 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
       const int min_slices = (c.bm * c.bn >= 128 * 128 && !widened) ? 16 : 8;
       int parts = std::min(num_cus / std::max(est, 1), nkb / min_slices);
       if (c.bm * c.bn < 128 * 128) parts = std::min(parts, 6);  // 64x2112x7168: 6 parts 3% faster than 4
+      // A fixup costs a few microseconds; short K ranges are not worth
+      // cutting (64x7168x2048: 11.6 us in 2 parts, 10.2 us whole).
+      if (nkb < 24) parts = 1;
       if (parts >= 2) sk = parts;
     } else if ((int64_t)est * nkb >= 24LL * num_cus) {
       sk = 1;
