@@ -789,26 +789,48 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
         constexpr int kFrag = T::FM * T::FN;
         constexpr int kPartBytes = kFrag * T::kThreads * 16;  // BM * BN * 4
         constexpr int kCacheSc1 = 16;                         // cache-policy bits: sc1
+        // 128x128 decode tiles first look whether every other contributor
+        // has already published: then this workgroup is the last one, keeps
+        // its own partial in registers and skips the store-and-wait round
+        // trip of its 64 KB partial (about 3 us), the usual case for the
+        // workgroup on the critical path.  Nobody waits for anybody either
+        // way.  (On 64x64 tiles the counter read costs as much as the 16 KB
+        // store it can save: measured 2-3% slower there.)
+        constexpr bool kEarly = kFrag <= 8 && T::kWaves <= 8 && T::BM * T::BN >= 128 * 128;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             uniform_ptr(p.workspace), (short)0, 2 * s.sk_slots * kPartBytes, 0x00020000);
         const int my_slot = 2 * run + slot;
-#pragma unroll
-        for (int f = 0; f < kFrag; ++f)
-          __builtin_amdgcn_raw_buffer_store_b128(acc[f / T::FN][f % T::FN], rs,
-                                                 my_slot * kPartBytes + f * T::kThreads * 16 + tid * 16, 0, kCacheSc1);
-        asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
-        __syncthreads();
         const int tr = t - dp_tiles;
         const int it_a = tr * nkb_total;
         const int w_lo = sk_owner(it_a), w_hi = sk_owner(it_a + nkb_total - 1);
-        if (tid == 0) {
-          const int old = __hip_atomic_fetch_add(&p.counters[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          last_flag = (old == w_hi - w_lo);
+        bool early = false;
+        if constexpr (kEarly) {
+          if (tid == 0)
+            last_flag = __hip_atomic_load(&p.counters[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == w_hi - w_lo;
+          __syncthreads();
+          early = last_flag;
         }
-        __syncthreads();
-        if (!last_flag) continue;
+        v4f own[kEarly ? kFrag : 1];
+        if (early) {
+#pragma unroll
+          for (int f = 0; f < (kEarly ? kFrag : 1); ++f) own[f] = acc[f / T::FN][f % T::FN];
+        } else {
+#pragma unroll
+          for (int f = 0; f < kFrag; ++f)
+            __builtin_amdgcn_raw_buffer_store_b128(acc[f / T::FN][f % T::FN], rs,
+                                                   my_slot * kPartBytes + f * T::kThreads * 16 + tid * 16, 0, kCacheSc1);
+          asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+          __syncthreads();
+          if (tid == 0) {
+            const int old = __hip_atomic_fetch_add(&p.counters[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last_flag = (old == w_hi - w_lo);
+          }
+          __syncthreads();
+          if (!last_flag) continue;
+        }
         // Sum the partials of runs w_lo .. w_hi (ascending K) into acc, in
-        // chunks of fragments with up to kG runs' loads in flight.
+        // chunks of fragments with up to kG runs' loads in flight; on the
+        // early path this workgroup's own run comes from registers.
         const int lo_slot = sk_start(w_lo) < it_a ? 1 : 0;  // run w_lo began in an earlier tile
         constexpr int kChunk = kFrag < 8 ? kFrag : 8;
         constexpr int kG = T::kWaves >= 16 ? 1 : (kFrag >= 32 ? 2 : 4);
@@ -822,12 +844,19 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
 #pragma unroll
             for (int q = 0; q < kG; ++q) {
               const int src = 2 * (w + q) + ((w + q) == w_lo ? lo_slot : 0);
+              const bool mine = kEarly && early && (w + q) == run;
 #pragma unroll
               for (int f = 0; f < kChunk; ++f)
-                v[q][f] = w + q <= w_hi
+                v[q][f] = (w + q <= w_hi && !mine)
                               ? __builtin_amdgcn_raw_buffer_load_b128(
                                     rs, src * kPartBytes + (f0 + f) * T::kThreads * 16 + tid * 16, 0, kCacheSc1)
                               : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+              if constexpr (kEarly) {
+                if (mine) {
+#pragma unroll
+                  for (int f = 0; f < kChunk; ++f) v[q][f] = own[f0 + f];
+                }
+              }
             }
 #pragma unroll
             for (int q = 0; q < kG; ++q)
