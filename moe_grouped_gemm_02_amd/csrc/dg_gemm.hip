@@ -1096,8 +1096,15 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
     // when they alone keep most CUs busy or K is long, else 64x64 tiles.
     const int t128 = tiles_of(128, 128);
     v = (rows > 64 && (10 * t128 >= 7 * num_cus || nkb >= 64)) ? 6 : 4;
+  } else if (tiles_of(256, 256) >= num_cus / 2) {
+    v = 0;
   } else {
-    v = tiles_of(256, 256) >= num_cus / 2 ? 0 : 1;
+    // Mid-size M (e.g. 1024 rows in all): 128-row tiles, 256 columns wide
+    // unless 128 columns fill the CUs' last round better (measured on the
+    // pages' all-valid masked rows: 1024x7168x2048 39.8 -> 31.1 us with
+    // 128x256, 1024x4096x7168 58.5 -> 53.1 us with 128x128).
+    auto fill = [&](int t) { return (double)t / (double)(cdiv(t, num_cus) * num_cus); };
+    v = fill(tiles_of(128, 256)) >= fill(tiles_of(128, 128)) ? 5 : 6;
   }
   // A quantised output needs whole 128-column blocks per tile: the 64-wide
   // decode tiles give way to the 128x128 one.
@@ -1119,7 +1126,9 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
   const int est = tiles_of(c.bm, c.bn);
   int sk = 0;  // 0: data-parallel, 1: equal runs, S >= 2: S parts per tile
   if (layout != kContiguous && nkb >= 2 && 10 * est < 7 * num_cus) {
-    if (c.bm <= 128 && rows <= 128) {
+    // K parts for 128-row (or smaller) tiles up to 1024 rows in all; beyond
+    // that, or when parts do not pay, equal runs for long K.
+    if (c.bm <= 128 && rows <= 1024) {
       // Shorter parts for the 128x128 tiles that stand in for 64-wide ones
       // (quantised output): fewer tiles, so more parts (64x4096x7168 fused:
       // 27.5 -> 24.2 us with 8 parts instead of 3).
@@ -1130,9 +1139,8 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
       // cutting (64x7168x2048: 11.6 us in 2 parts, 10.2 us whole).
       if (nkb < 24) parts = 1;
       if (parts >= 2) sk = parts;
-    } else if ((int64_t)est * nkb >= 24LL * num_cus) {
-      sk = 1;
     }
+    if (sk == 0 && rows > 128 && (int64_t)est * nkb >= 24LL * num_cus) sk = 1;
   }
   const int fs = forced_stream_k();
   if (fs >= 0) sk = fs;
@@ -1190,6 +1198,7 @@ hipError_t launch_gemm(int layout, const GemmParams& p0, const GemmConfig& cfg,
       case 1: return launch_layout<TileP128, kScaleUE8M0>(layout, p, s, cfg.grid, stream);
       case 4: return launch_layout<TileS64, kScaleUE8M0>(layout, p, s, cfg.grid, stream);
       case 6: return launch_layout<TileP128w8, kScaleUE8M0>(layout, p, s, cfg.grid, stream);
+      case 5: return launch_layout<TileW128, kScaleUE8M0>(layout, p, s, cfg.grid, stream);
       default: return hipErrorInvalidValue;
     }
   }

@@ -39,7 +39,9 @@ struct GemmParams {
 };
 
 // Tile variants built with UE8M0 scales.
-inline bool ue8m0_variant_built(int variant) { return variant == 0 || variant == 1 || variant == 4 || variant == 6; }
+inline bool ue8m0_variant_built(int variant) {
+  return variant == 0 || variant == 1 || variant == 4 || variant == 5 || variant == 6;
+}
 
 // Tile configuration chosen on the host (deterministically, from the shape).
 struct GemmConfig {
