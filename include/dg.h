@@ -181,6 +181,31 @@ int dg_grouped_masked_qout(const uint8_t* a, const float* sfa, const uint8_t* b,
                            int num_groups, int m_max, int n, int k, int expected_m, int64_t ld_sfa,
                            int64_t ld_dsf, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * K-axis grouped GEMM (the weight-gradient GEMM of MoE training): the tokens
+ * of all experts are concatenated along K, and group g owns the K range
+ * [k_offsets[g], k_offsets[g+1]).  The pages name grouping along K next to
+ * grouping along M ("DeepGEMM: efficient BLAS kernel library on GPU",
+ * yfxerp.com, section 3.2) and say no more; reading taken here: both operands
+ * are activation-like and carry the activation quantiser's 1x128 scales along
+ * K, so
+ *   D_g[m][n] = bf16( sum_{kb in group g} P_kb[m][n] * (sfa[kb][m] * sfb[kb][n]) ).
+ *   a   [m][k] e4m3, sfa [k/128][ld_sfa] fp32 (ld_sfa >= m, a multiple of 4)
+ *   b   [n][k] e4m3, sfb [k/128][ld_sfb] fp32 (ld_sfb >= n, a multiple of 4):
+ *       one scale per row of B and 128-wide K slice (dg_quant_1x128 of B)
+ *   d   [num_groups][m][n] bf16
+ *   k_offsets [num_groups + 1] int32 (device): 0 = k_offsets[0] <= ... <=
+ *       k_offsets[num_groups] = k, multiples of 128 (precondition; values are
+ *       clamped to [0, k] and rounded down to a slice, so nothing is read out
+ *       of bounds for any content).  An empty group writes zeros.
+ * Rules as for dg_fp8_gemm_nt with lda = ldb = k and ldd = n, plus n % 8 == 0.
+ * Needs no workspace (pass NULL, 0).  Data-parallel over (group, M tile,
+ * N tile) units.
+ */
+int dg_k_grouped_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb, uint16_t* d,
+                    const int32_t* k_offsets, int num_groups, int m, int n, int k, int64_t ld_sfa,
+                    int64_t ld_sfb, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ----------------------------------------------------------- quantisers -- */
 
 /*
@@ -266,7 +291,7 @@ int64_t dg_get_ue8m0_sfb_leading_dim(int n);
 const char* dg_get_last_error_string(void);
 
 /* Human-readable description of the tile configuration the library would
- * choose for a GEMM (layout 0 = dense, 1 = contiguous, 2 = masked, plus 8 for
+ * choose for a GEMM (layout 0 = dense, 1 = contiguous, 2 = masked, 3 = K-grouped, plus 8 for
  * the *_qout entry points; m is M, M_total or M_max; expected_m is the masked
  * layout's hint, 0 otherwise),
  * written into buf (NUL-terminated, truncated to len).  Returns DG_SUCCESS or

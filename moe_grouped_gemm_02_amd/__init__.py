@@ -40,6 +40,7 @@ _SIGNATURES = {
     "dg_fp8_gemm_nt_qout": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _L, _L, _L, _P, _S, _P]),
     "dg_grouped_contiguous_qout": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _L, _P, _S, _P]),
     "dg_grouped_masked_qout": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _P, _S, _P]),
+    "dg_k_grouped_nt": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _L, _P, _S, _P]),
     "dg_quant_1x128": (_I, [_P, _P, _P, _I, _I, _L, _I, _P]),
     "dg_quant_128x128": (_I, [_P, _P, _P, _I, _I, _I, _P]),
     "dg_quant_1x128_ue8m0": (_I, [_P, _P, _P, _I, _I, _L, _I, _P]),
@@ -60,7 +61,7 @@ for _name, (_res, _args) in _SIGNATURES.items():
 
 EXPORTED = tuple(_SIGNATURES)
 
-LAYOUT_DENSE, LAYOUT_CONTIGUOUS, LAYOUT_MASKED = 0, 1, 2
+LAYOUT_DENSE, LAYOUT_CONTIGUOUS, LAYOUT_MASKED, LAYOUT_K_GROUPED = 0, 1, 2, 3
 
 
 class DGError(RuntimeError):
@@ -297,6 +298,28 @@ def dg_grouped_masked_qout(a, sfa, b, sfb, d, dq, dsf, masked_m, expected_m=0, w
         _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), _ptr(dq), _ptr(dsf), _ptr(masked_m), groups, m_max, n, k,
         int(expected_m), sfa.shape[2], ld_dsf, _ptr(workspace), _ws(workspace), _stream(d)))
     return d, dq, dsf
+
+
+def dg_k_grouped_nt(a, sfa, b, sfb, d, k_offsets, workspace=None):
+    """K-grouped GEMM: a [M][K], b [N][K] e4m3 with 1x128 scales sfa [K/128][ld_a],
+    sfb [K/128][ld_b]; d [G][M][N]; k_offsets [G+1] int32 (device)."""
+    _expect(a, "a", _U8, 2), _expect(b, "b", _U8, 2), _expect(d, "d", _BF, 3)
+    _expect(sfa, "sfa", (torch.float32,), 2), _expect(sfb, "sfb", (torch.float32,), 2)
+    _expect(k_offsets, "k_offsets", (torch.int32,), 1)
+    m, k = a.shape
+    n = b.shape[0]
+    groups = d.shape[0]
+    if b.shape[1] != k or tuple(d.shape) != (groups, m, n) or k_offsets.shape[0] != groups + 1:
+        raise ValueError("shape mismatch between a, b, d and k_offsets")
+    if sfa.shape[0] != k // 128 or sfb.shape[0] != k // 128:
+        raise ValueError("scale shapes must be sfa [K/128][ld_a] and sfb [K/128][ld_b]")
+    for t, nm in ((a, "a"), (b, "b"), (d, "d"), (k_offsets, "k_offsets")):
+        _contig(t, nm)
+    _row_major(sfa, "sfa"), _row_major(sfb, "sfb")
+    _check("dg_k_grouped_nt", _lib.dg_k_grouped_nt(
+        _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), _ptr(k_offsets), groups, m, n, k,
+        sfa.stride(0), sfb.stride(0), _ptr(workspace), _ws(workspace), _stream(d)))
+    return d
 
 
 # ------------------------------------------------------------- quantisers --

@@ -61,7 +61,12 @@ bool debug_enabled() {
 }
 
 const char* layout_name(int layout) {
-  return layout == dg::kDense ? "dense" : (layout == dg::kContiguous ? "contiguous" : "masked");
+  switch (layout) {
+    case dg::kDense: return "dense";
+    case dg::kContiguous: return "contiguous";
+    case dg::kMasked: return "masked";
+    default: return "k_grouped";
+  }
 }
 
 // Shared checks for the three GEMM entry points.  rows = the rows of the
@@ -105,6 +110,8 @@ int run_gemm(int layout, dg::GemmParams& p, int rows, int groups, void* ws, size
   if (cus < 0) return fail(DG_ERR_HIP, "cannot query the device's compute-unit count");
   const bool qout = p.dq != nullptr;
   const dg::GemmConfig cfg = dg::choose_config(layout, rows, p.n, p.k, groups, cus, expected_m, qout);
+  if (layout == dg::kKGrouped && !dg::kgrouped_variant_built(cfg.variant))
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "tile variant %d is not built for the K-grouped layout", cfg.variant);
   if (p.sf_ue8m0 && !dg::ue8m0_variant_built(cfg.variant))
     return fail(DG_ERR_UNSUPPORTED_SHAPE, "tile variant %d is not built for UE8M0 scales", cfg.variant);
   if (qout && !dg::variant_quantises_output(cfg.variant))
@@ -226,6 +233,29 @@ int masked_impl(const uint8_t* a, const void* sfa, const uint8_t* b, const void*
   return run_gemm(dg::kMasked, p, m_max, num_groups, workspace, workspace_bytes, stream, expected_m);
 }
 
+int k_grouped_impl(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb, uint16_t* d,
+                   const int32_t* k_offsets, int num_groups, int m, int n, int k, int64_t ld_sfa,
+                   int64_t ld_sfb, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_groups < 1) return fail(DG_ERR_INVALID_VALUE, "num_groups must be >= 1");
+  int st = check_gemm_common(a, sfa, b, sfb, d, m, n, k, k, k, n, ld_sfa);
+  if (st != DG_SUCCESS) return st;
+  if (!k_offsets) return fail(DG_ERR_INVALID_VALUE, "null k_offsets");
+  if (n % 8) return fail(DG_ERR_MISALIGNED, "n must be a multiple of 8 (rows of d are packed)");
+  if (ld_sfb < n || ld_sfb < 4) return fail(DG_ERR_INVALID_VALUE, "ld_sfb=%lld smaller than n (%d) or 4", (long long)ld_sfb, n);
+  if (ld_sfb % 4) return fail(DG_ERR_MISALIGNED, "ld_sfb must be a multiple of 4");
+  if ((int64_t)(k / 128) * ld_sfb * 4 >= ((int64_t)1 << 32)) return fail(DG_ERR_UNSUPPORTED_SHAPE, "sfb of 4 GiB or more");
+  if ((int64_t)num_groups * ((m + 63) / 64) * ((n + 63) / 64) >= ((int64_t)1 << 31))
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many output tiles");
+  if (m == 0 || n == 0) return ok();
+  dg::GemmParams p{};
+  p.a = a; p.b = b; p.d = d; p.k_offsets = k_offsets;
+  p.sfa = sfa; p.sfb = sfb; p.ld_sfb = ld_sfb;
+  p.m = m; p.n = n; p.k = k; p.num_groups = num_groups;
+  p.lda = k; p.ldb = k; p.ldd = n; p.ld_sfa = ld_sfa;
+  p.d_gstride = (int64_t)m * n;
+  return run_gemm(dg::kKGrouped, p, m, num_groups, workspace, workspace_bytes, stream);
+}
+
 int quant_1x128_impl(const uint16_t* x, uint8_t* q, void* sf, int rows, int cols, int64_t ld_sf,
                      int num_groups, bool pow2, void* stream) {
   if (rows < 0 || cols < 0 || num_groups < 1) return fail(DG_ERR_INVALID_VALUE, "bad sizes (rows=%d cols=%d groups=%d)", rows, cols, num_groups);
@@ -336,6 +366,13 @@ int dg_grouped_masked_qout(const uint8_t* a, const float* sfa, const uint8_t* b,
                      workspace, workspace_bytes, stream, false, &q);
 }
 
+int dg_k_grouped_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb, uint16_t* d,
+                    const int32_t* k_offsets, int num_groups, int m, int n, int k, int64_t ld_sfa,
+                    int64_t ld_sfb, void* workspace, size_t workspace_bytes, void* stream) {
+  return k_grouped_impl(a, sfa, b, sfb, d, k_offsets, num_groups, m, n, k, ld_sfa, ld_sfb, workspace,
+                        workspace_bytes, stream);
+}
+
 int dg_quant_1x128(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
                    int64_t ld_sf, int num_groups, void* stream) {
   return quant_1x128_impl(x, q, sf, rows, cols, ld_sf, num_groups, false, stream);
@@ -406,7 +443,7 @@ int dg_describe_config(int layout, int m, int n, int k, int num_groups, int expe
                        int num_cus, char* buf, size_t len) {
   const bool qout = (layout & 8) != 0;  // configuration of the *_qout entry points
   layout &= ~8;
-  if (layout < dg::kDense || layout > dg::kMasked || m < 0 || n < 0 || k < 0 ||
+  if (layout < dg::kDense || layout > dg::kKGrouped || m < 0 || n < 0 || k < 0 ||
       num_groups < 1 || expected_m < 0 || num_cus < 1 || !buf || len == 0)
     return fail(DG_ERR_INVALID_VALUE, "bad arguments to dg_describe_config");
   const dg::GemmConfig c = dg::choose_config(layout, m, n, k, num_groups, num_cus, expected_m, qout);

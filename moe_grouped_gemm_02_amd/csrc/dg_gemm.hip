@@ -192,7 +192,9 @@ __device__ __forceinline__ int clamp_rows(int v, int hi) { return v < 0 ? 0 : (v
 
 // Scale formats.  UE8M0 exponents are bytes; the scale pointers keep the
 // fp32 type and group strides count elements of the format in use.
-constexpr int kScaleF32 = 0, kScaleUE8M0 = 1;
+// kScaleRowB (K-grouped layout): fp32 activation-style 1x128 scales on both
+// operands, the B scales per row of B: [K/128][ld_sfb].
+constexpr int kScaleF32 = 0, kScaleUE8M0 = 1, kScaleRowB = 2;
 template <int SF>
 __device__ __forceinline__ const float* scale_ptr(const float* base, int64_t offset) {
   if constexpr (SF == kScaleUE8M0)
@@ -225,7 +227,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
     for (int g = 0; g < p.num_groups; ++g)
       m_tiles += (clamp_rows(p.masked_m[g], p.m) + T::BM - 1) / T::BM;
   }
-  const int tiles = m_tiles * s.n_tiles;
+  // K-grouped: every group has the same M x N tiles.
+  const int tiles = (LAYOUT == kKGrouped ? p.num_groups : 1) * m_tiles * s.n_tiles;
   const int G = gridDim.x;
   // Stream-K.  The tiles of the whole waves of G run one per workgroup
   // (data-parallel); the (tile, K slice) iterations of the remaining tiles
@@ -292,9 +295,20 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
     } else {
       break;
     }
+    int g = 0;
+    if (LAYOUT == kKGrouped) {
+      // Group g owns the K range [k_offsets[g], k_offsets[g+1]) (128-aligned
+      // by contract; clamped and rounded down here, so any value is safe).
+      const int per_group = m_tiles * s.n_tiles;
+      g = t / per_group;
+      t -= g * per_group;
+      const int k_lo = min(max(p.k_offsets[g], 0), p.k);
+      const int k_hi = min(max(p.k_offsets[g + 1], 0), p.k);
+      kb0 = __builtin_amdgcn_readfirstlane(k_lo >> 7);
+      kb1 = __builtin_amdgcn_readfirstlane(max(k_lo >> 7, k_hi >> 7));
+    }
     int mt, nt;
     raster(t, m_tiles, s.n_tiles, s.group_m, mt, nt);
-    int g = 0;
     if (LAYOUT == kMasked) {
       int before = 0;
       for (g = 0; g < p.num_groups - 1; ++g) {
@@ -313,6 +327,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
     uint16_t* D = p.d;
     uint8_t* DQ = p.dq;
     float* DSF = p.dsf;
+    if (LAYOUT == kKGrouped) D += (int64_t)g * p.d_gstride;
     if (LAYOUT == kMasked) {
       rows_valid = clamp_rows(p.masked_m[g], p.m);
       A += (int64_t)g * p.a_gstride;
@@ -412,6 +427,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
               // Activation scales of the slice: rows m0 .. m0 + 4*63 + 3.
               const int r4 = min(m0 + 4 * lane, (int)p.ld_sfa - 4);
               dma16(stage_lds + T::kSOffInstr * 1024, SA, (uint32_t)(kb * p.ld_sfa + r4) * 4u);
+            } else if (SF == kScaleRowB && wave == 1) {
+              // Row scales of B: columns n0 .. n0 + 4*63 + 3 of the slice.
+              const int c4 = min(n0 + 4 * lane, (int)p.ld_sfb - 4);
+              dma16(stage_lds + T::kSBOff, SB, (uint32_t)(kb * p.ld_sfb + c4) * 4u);
             } else if (wave == 1) {
               // Weight scales of the slice for the tile's column blocks (lane l:
               // block cb_first + l; lanes past the last block repeat it).
@@ -482,6 +501,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
             if constexpr (q * T::FN / T::kIssue == j) issue_piece(kb, buf, qc);
           });
         };
+        static_assert(SF == kScaleUE8M0, "the late-barrier loop is the power-of-two-scale one");
         if (nkb > 0) issue_stage(kb_at(0), 0);
         if (nkb > 1) {
           issue_stage(kb_at(1), 1);
@@ -491,7 +511,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
           wait_vm<0>();
         }
         barrier_all();
-        if constexpr (SF == kScaleUE8M0) {
+        {
           // Exponent bytes: A rows at kSOff, the weight blocks (cb_first & ~3)
           // onwards at kSBOff.
           auto ld_e = [&](const uint8_t* sp, int i) { return (int)sp[T::kSOff + wm * T::TM + i * 16 + fr]; };
@@ -547,84 +567,6 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
                   issue_after(kb_next, it & 1, jc);
                 }
               });
-            });
-          }
-        } else {
-          auto ld_s = [&](const uint8_t* sp, int i) {
-            return *reinterpret_cast<const float4*>(sp + T::kSOff + (wm * T::TM + i * 16 + 4 * kg) * 4);
-          };
-          auto ld_sb = [&](const uint8_t* sp, int j) {
-            return reinterpret_cast<const float*>(sp + T::kSBOff)[col_block(j) - cb_first];
-          };
-          v8i bfrag[T::FN];
-          float sbv[T::FN];
-#pragma unroll
-          for (int j = 0; j < T::FN; ++j) {
-            bfrag[j] = ld_b(smem, j);
-            if (!T::kOneSB || j == 0) sbv[j] = ld_sb(smem, j);
-          }
-          v8i afrag = ld_a(smem, 0);
-          float4 s4 = ld_s(smem, 0);
-          for (int it = 0; it < nkb; ++it) {
-            const uint8_t* st = smem + (it & 1) * T::kStageBytes;
-            const uint8_t* sn = smem + ((it + 1) & 1) * T::kStageBytes;
-            // The DMA after the barrier loads slice it + 2; in the last two
-            // slices it reloads slice it into its own, no longer read, buffer
-            // (identical bytes), which keeps the loop free of branches that
-            // would let the compiler sink the MFMAs below the barrier.
-            const int kb_next = kb_at(it + 2 < nkb ? it + 2 : it);
-            static_for<T::FM>([&](auto ic) {
-              constexpr int i = decltype(ic)::value;
-              if constexpr (i == T::FM - 1) {
-                __builtin_amdgcn_sched_barrier(0);
-                wait_vm<0>();
-                barrier_all();
-              }
-              __builtin_amdgcn_sched_barrier(0);  // row by row, as above
-              const float4 s_cur = s4;
-              float sb_cur[T::FN];
-#pragma unroll
-              for (int j = 0; j < T::FN; ++j) sb_cur[j] = sbv[T::kOneSB ? 0 : j];
-              v4f part[T::FN];
-              static_for<T::FN>([&](auto jc) {
-                constexpr int j = decltype(jc)::value;
-                part[j] = mfma_fp8_slice(afrag, bfrag[j]);
-                if constexpr (i == T::FM - 1) {
-                  __builtin_amdgcn_sched_barrier(0);
-                  bfrag[j] = ld_b(sn, j);
-                  if (!T::kOneSB || j == 0) sbv[j] = ld_sb(sn, j);
-                  issue_after(kb_next, it & 1, jc);
-                }
-              });
-              // The next row's A fragment and activation scales (the next
-              // slice's first row after the last), read while the FMAs run.
-              if constexpr (i + 1 < T::FM) {
-                afrag = ld_a(st, i + 1);
-                s4 = ld_s(st, i + 1);
-              } else {
-                afrag = ld_a(sn, 0);
-                s4 = ld_s(sn, 0);
-              }
-              const float sa[4] = {s_cur.x, s_cur.y, s_cur.z, s_cur.w};
-              if constexpr (T::kOneSB) {
-                float sc[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sc[e] = sa[e] * sb_cur[0];
-#pragma unroll
-                for (int j = 0; j < T::FN; ++j)
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(part[j][e], sc[e], acc[i][j][e]);
-              } else {
-#pragma unroll
-                for (int j = 0; j < T::FN; ++j)
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(part[j][e], sa[e] * sb_cur[j], acc[i][j][e]);
-              }
-              // Pin the row's FMAs here: the wave-dependent scale DMA after
-              // the barrier is a branch, below which the compiler would
-              // otherwise sink every row's FMAs (keeping all partials live).
-#pragma unroll
-              for (int j = 0; j < T::FN; ++j) asm volatile("" : "+v"(acc[i][j]));
             });
           }
         }
@@ -700,10 +642,16 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
               }
             });
           } else {
+            // One weight scale for all the wave's columns when they sit in one
+            // 128-column block; row scales of B (K-grouped) differ per column.
+            constexpr bool kOneSB = T::kOneSB && SF != kScaleRowB;
             float sbw = 0.0f;
             float sbv[T::FN];
             const float* sbs = reinterpret_cast<const float*>(st + T::kSBOff);
-            if (T::kOneSB) {
+            if constexpr (SF == kScaleRowB) {
+  #pragma unroll
+              for (int j = 0; j < T::FN; ++j) sbv[j] = sbs[wn * T::TN + j * 16 + fr];  // this lane's output column
+            } else if (kOneSB) {
               const int cb = min((n0 + wn * T::TN) >> 7, n_blocks - 1);
               sbw = sbs[cb - cb_first];
             } else {
@@ -766,12 +714,12 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
               const float sa[4] = {s_cur.x, s_cur.y, s_cur.z, s_cur.w};
               float sc[4];
   #pragma unroll
-              for (int e = 0; e < 4; ++e) sc[e] = T::kOneSB ? sa[e] * sbw : 0.0f;
+              for (int e = 0; e < 4; ++e) sc[e] = kOneSB ? sa[e] * sbw : 0.0f;
   #pragma unroll
               for (int j = 0; j < T::FN; ++j)
   #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                  acc[i][j][e] = fmaf(part[cur][j][e], T::kOneSB ? sc[e] : sa[e] * sbv[j], acc[i][j][e]);
+                  acc[i][j][e] = fmaf(part[cur][j][e], kOneSB ? sc[e] : sa[e] * sbv[j], acc[i][j][e]);
             });
           }
         }
@@ -1042,6 +990,13 @@ hipError_t launch_layout(int layout, const GemmParams& p, const Schedule& s, int
   }
 }
 
+// K-grouped layout: data-parallel, row scales on B.
+template <class T>
+hipError_t launch_kgrouped(const GemmParams& p, const Schedule& s, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_kernel<T, kKGrouped, false, kScaleRowB>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
+  return hipGetLastError();
+}
+
 int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // Stream-K partial slots are addressed with 32-bit offsets: 2 * grid slots of
@@ -1088,7 +1043,7 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
   const int nkb = k / kBlockK;
   const bool hinted = layout == kMasked && expected_m > 0 && expected_m < m;
   const int rows = hinted ? expected_m : m;
-  const int gmul = layout == kMasked ? groups : 1;
+  const int gmul = (layout == kMasked || layout == kKGrouped) ? groups : 1;
   auto tiles_of = [&](int bm, int bn) { return cdiv(rows, bm) * gmul * cdiv(n, bn); };
   int v;
   if (rows <= 128) {
@@ -1125,7 +1080,7 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
   // estimate uses the hinted rows for the masked layout.
   const int est = tiles_of(c.bm, c.bn);
   int sk = 0;  // 0: data-parallel, 1: equal runs, S >= 2: S parts per tile
-  if (layout != kContiguous && nkb >= 2 && 10 * est < 7 * num_cus) {
+  if (layout != kContiguous && layout != kKGrouped && nkb >= 2 && 10 * est < 7 * num_cus) {
     // K parts for 128-row (or smaller) tiles up to 1024 rows in all; beyond
     // that, or when parts do not pay, equal runs for long K.
     if (c.bm <= 128 && rows <= 1024) {
@@ -1144,7 +1099,7 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
   }
   const int fs = forced_stream_k();
   if (fs >= 0) sk = fs;
-  if (layout == kContiguous || nkb < 2) sk = 0;
+  if (layout == kContiguous || layout == kKGrouped || nkb < 2) sk = 0;
   if (sk >= 2) sk = std::min(sk, nkb);
   c.stream_k = sk > 0 ? 1 : 0;
   c.sk_split = sk >= 2 ? sk : 0;
@@ -1186,7 +1141,7 @@ hipError_t launch_gemm(int layout, const GemmParams& p0, const GemmConfig& cfg,
   GemmParams p = p0;
   Schedule s{};
   s.n_tiles = cdiv(p.n, cfg.bn);
-  s.m_tiles = cfg.tiles / s.n_tiles;
+  s.m_tiles = layout == kKGrouped ? cdiv(p.m, cfg.bm) : cfg.tiles / s.n_tiles;  // K-grouped: per group
   s.tiles = cfg.tiles;
   s.stream_k = cfg.stream_k;
   s.sk_split = cfg.sk_split;
@@ -1196,6 +1151,15 @@ hipError_t launch_gemm(int layout, const GemmParams& p0, const GemmConfig& cfg,
   if (cfg.stream_k)
     p.counters = reinterpret_cast<int*>(reinterpret_cast<char*>(p.workspace) +
                                         2 * (size_t)cfg.sk_slots * cfg.bm * cfg.bn * sizeof(float));
+  if (layout == kKGrouped) {
+    switch (cfg.variant) {
+      case 0: return launch_kgrouped<TileP256>(p, s, cfg.grid, stream);
+      case 4: return launch_kgrouped<TileS64>(p, s, cfg.grid, stream);
+      case 5: return launch_kgrouped<TileW128>(p, s, cfg.grid, stream);
+      case 6: return launch_kgrouped<TileP128w8>(p, s, cfg.grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (p.sf_ue8m0) {  // UE8M0 instances: the tiles the heuristic picks
     switch (cfg.variant) {
       case 0: return launch_layout<TileP256, kScaleUE8M0>(layout, p, s, cfg.grid, stream);

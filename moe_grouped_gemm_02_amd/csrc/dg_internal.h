@@ -6,7 +6,7 @@
 
 namespace dg {
 
-enum Layout : int { kDense = 0, kContiguous = 1, kMasked = 2 };
+enum Layout : int { kDense = 0, kContiguous = 1, kMasked = 2, kKGrouped = 3 };
 
 // Everything a GEMM kernel needs; group strides are in elements.
 struct GemmParams {
@@ -17,6 +17,7 @@ struct GemmParams {
   uint16_t* d;
   const int32_t* m_indices;  // contiguous layout only
   const int32_t* masked_m;   // masked layout only
+  const int32_t* k_offsets;  // K-grouped layout only: [G + 1] K offsets of the groups
   float* workspace;          // stream-K partials (fp32), may be null
   int* counters;             // stream-K arrival counters, may be null
   int m;                     // dense: M; contiguous: M_total; masked: M_max
@@ -27,7 +28,8 @@ struct GemmParams {
   int64_t a_gstride, sfa_gstride, b_gstride, sfb_gstride, d_gstride;
   // UE8M0 scales (power-of-two exponent bytes): sfa/sfb point at bytes, the
   // weight exponents are MN-major [G][K/128][ld_sfb], and the scale group
-  // strides count bytes.
+  // strides count bytes.  K-grouped layout: sfb is fp32 [K/128][ld_sfb], one
+  // scale per row of B and 128-wide K slice.
   int sf_ue8m0;
   int64_t ld_sfb;
   // Quantised copy of the output (null: none): e4m3 codes [G][rows][n] and
@@ -39,6 +41,11 @@ struct GemmParams {
 };
 
 // Tile variants built with UE8M0 scales.
+// Tile variants built for the K-grouped layout.
+inline bool kgrouped_variant_built(int variant) {
+  return variant == 0 || variant == 4 || variant == 5 || variant == 6;
+}
+
 inline bool ue8m0_variant_built(int variant) {
   return variant == 0 || variant == 1 || variant == 4 || variant == 5 || variant == 6;
 }
