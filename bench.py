@@ -105,7 +105,7 @@ def parse_args(argv=None):
 def select_workloads(name):
     import synth
     wls = synth.workloads()
-    extra = synth.pages_workloads()
+    extra = synth.pages_workloads() + synth.extra_workloads()
     if name == "decode128":
         return [w for w in wls if w.layout == "dense" and w.m == 128]
     if name == "all":
@@ -130,7 +130,10 @@ class Prepared:
         sf_dtype = torch.uint8 if ue else torch.float32
         g, n, k = wl.groups, wl.n, wl.k
         dev = "cuda"
-        if wl.layout == "dense":
+        kg = wl.layout == "k_grouped"
+        if kg and ue:
+            raise SystemExit("the K-grouped GEMM takes fp32 scales only")
+        if wl.layout in ("dense", "k_grouped"):
             self.m_rows, a_shape = wl.m, (wl.m, k)
         elif wl.layout == "contiguous":
             self.m_rows, a_shape = g * wl.m, (g * wl.m, k)
@@ -141,21 +144,27 @@ class Prepared:
         self.a = torch.empty(a_shape, dtype=torch.uint8, device=dev)
         ld = dg.dg_get_sf_leading_dim(self.m_rows)
         self.sfa = torch.empty(((g,) if wl.layout == "masked" else ()) + (k // 128, ld), dtype=sf_dtype, device=dev)
-        b_shape = (n, k) if wl.layout == "dense" else (g, n, k)
+        b_shape = (n, k) if wl.layout in ("dense", "k_grouped") else (g, n, k)
         xb = torch.from_numpy(synth.bf16_normal(b_shape, wl.seed_b).view(np.int16)).to(dev)
         qb = torch.empty(b_shape, dtype=torch.uint8, device=dev)
-        sfb_shape = (k // 128, dg.dg_get_ue8m0_sfb_leading_dim(n)) if ue else ((n + 127) // 128, k // 128)
-        sfb = torch.empty(((g,) if wl.layout != "dense" else ()) + sfb_shape, dtype=sf_dtype, device=dev)
-        (dg.dg_quant_128x128_ue8m0 if ue else dg.dg_quant_128x128)(xb, qb, sfb)
+        if kg:  # both operands activation-like: 1x128 scales along K
+            sfb = torch.empty((k // 128, dg.dg_get_sf_leading_dim(n)), dtype=torch.float32, device=dev)
+            dg.dg_quant_1x128(xb, qb, sfb)
+        else:
+            sfb_shape = (k // 128, dg.dg_get_ue8m0_sfb_leading_dim(n)) if ue else ((n + 127) // 128, k // 128)
+            sfb = torch.empty(((g,) if wl.layout != "dense" else ()) + sfb_shape, dtype=sf_dtype, device=dev)
+            (dg.dg_quant_128x128_ue8m0 if ue else dg.dg_quant_128x128)(xb, qb, sfb)
         del xb
         set_bytes = qb.numel() + sfb.numel() * sfb.element_size()
         copies = max(1, math.ceil(2 * MALL_BYTES / set_bytes)) if set_bytes < 2 * MALL_BYTES else 1
         copies = min(copies, 64)
         self.b = [qb] + [qb.clone() for _ in range(copies - 1)]
         self.sfb = [sfb] + [sfb.clone() for _ in range(copies - 1)]
-        self.d = torch.empty(((g,) if wl.layout == "masked" else ()) + (self.m_rows, n), dtype=torch.int16, device=dev)
+        self.d = torch.empty(((g,) if wl.layout in ("masked", "k_grouped") else ()) + (self.m_rows, n),
+                             dtype=torch.int16, device=dev)
         self.mi = None
         self.mm = None
+        self.koffs = None
         if wl.layout == "contiguous":
             self.mi = torch.from_numpy(synth.contiguous_m_indices([wl.m] * g)).to(dev)
             self.m_valid = g * wl.m
@@ -165,12 +174,16 @@ class Prepared:
             self.m_valid = int(mm.sum())
         else:
             self.m_valid = wl.m
+        if kg:
+            self.koffs = torch.from_numpy(synth.k_group_offsets(wl)).to(dev)
         ws = dg.dg_get_workspace_size(self.m_rows, n, k, g)
         self.ws = torch.zeros(ws, dtype=torch.uint8, device=dev) if ws else None
         self.flops = algorithmic_flops(self.m_valid, n, k)
         self.bytes = algorithmic_bytes(self.m_valid, n, k, g)
+        if kg:  # A and B once, G output matrices
+            self.bytes = float(wl.m * k + n * k + 2 * g * wl.m * n)
         self.sf_bytes = scale_bytes(self.m_valid, n, k, g, scales)
-        layout_id = {"dense": 0, "contiguous": 1, "masked": 2}[wl.layout]
+        layout_id = {"dense": 0, "contiguous": 1, "masked": 2, "k_grouped": 3}[wl.layout]
         self.expected_m = self.m_valid // g if wl.layout == "masked" else 0
         self.config = dg.dg_describe_config(layout_id, self.m_rows, n, k, g, dg.dg_get_num_cus(), self.expected_m)
         # One kernel instance per (tile variant, layout, stream-K or not): the
@@ -181,7 +194,7 @@ class Prepared:
         sfx = "_ue8m0" if ue else ""
         self._quant_a = getattr(dg, "dg_quant_1x128" + sfx)
         self._gemm = getattr(dg, {"dense": "dg_fp8_gemm_nt", "contiguous": "dg_grouped_contiguous",
-                                  "masked": "dg_grouped_masked"}[wl.layout] + sfx)
+                                  "masked": "dg_grouped_masked", "k_grouped": "dg_k_grouped_nt"}[wl.layout] + sfx)
 
     def quant(self, dg):
         self._quant_a(self.x, self.a, self.sfa)
@@ -192,6 +205,8 @@ class Prepared:
             self._gemm(self.a, self.sfa, b, sfb, self.d, workspace=self.ws)
         elif self.wl.layout == "contiguous":
             self._gemm(self.a, self.sfa, b, sfb, self.d, self.mi, workspace=self.ws)
+        elif self.wl.layout == "k_grouped":
+            self._gemm(self.a, self.sfa, b, sfb, self.d, self.koffs)
         else:
             self._gemm(self.a, self.sfa, b, sfb, self.d, self.mm, expected_m=self.expected_m, workspace=self.ws)
 
@@ -511,7 +526,7 @@ def main(argv=None):
 
     if args.launches_only:
         import synth
-        wl = {w.name: w for w in synth.workloads() + synth.pages_workloads()}[args.launches_only]
+        wl = {w.name: w for w in synth.workloads() + synth.pages_workloads() + synth.extra_workloads()}[args.launches_only]
         p = Prepared(dg, torch, wl, args.scales)
         for r in range(args.reps):
             p.quant(dg)

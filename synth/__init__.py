@@ -121,6 +121,22 @@ def workloads():
     return out
 
 
+def extra_workloads():
+    """Shapes beyond the pages' tables: the K-grouped weight-gradient GEMM of
+    an 8-expert MoE layer, M = 7168 (hidden) x N = 2048 (expert
+    intermediate), 8192 tokens in unequal 128-aligned groups (one empty), and
+    the same with equal groups."""
+    return [Workload("k_grouped_g8_m7168_n2048_k8192", "k_grouped", 7168, 2048, 8192, groups=8, number=6,
+                     extra={"tokens": [1024, 640, 1536, 0, 1152, 2048, 896, 896]}),
+            Workload("k_grouped_g8_m7168_n2048_k8192_equal", "k_grouped", 7168, 2048, 8192, groups=8, number=6,
+                     extra={"tokens": [1024] * 8})]
+
+
+def k_group_offsets(wl: "Workload") -> np.ndarray:
+    """[G + 1] int32 K offsets of a K-grouped workload's token groups."""
+    return np.concatenate([[0], np.cumsum(wl.extra["tokens"])]).astype(np.int32)
+
+
 def pages_workloads():
     """The rows of the pages' performance tables (DeepGEMM project introduction,
     section Performance) not already among workloads(): dense M = 64 at the
