@@ -23,19 +23,25 @@
 //   Tiles are row-major with 128-byte rows and the 16-byte chunk c of row r
 //   stored at position c ^ (r % 8), so 8 lanes reading 8 consecutive rows at
 //   one K offset touch 8 distinct 16-byte bank groups.
-// * Persistent workgroups (grid sized to the CU count) walk the work units;
-//   units that run at the same time on one XCD (workgroup id mod 8) are given
-//   neighbouring tiles so they share A and B lines in that XCD's L2.
-// * Split-K (for shapes with fewer tiles than CUs): each unit computes a K
-//   range of one tile and writes an fp32 partial; the last unit of a tile to
-//   finish (arrival counter) sums the partials in split order - a fixed order,
-//   so results are bit-identical run to run - and stores bf16.  Each XCD is
-//   given the tiles of one K range, so the activation slices of that range,
-//   which every tile reads, stay in the XCD's L2.
-//
-// The unaligned tile widths (BN not a power of two) follow the pages' point
-// that power-of-two blocks can leave SMs idle (project introduction,
-// Optimisations, "unaligned block sizes").
+// * Persistent workgroups (grid sized to the CU count; two per CU for the
+//   64x64 tiles) walk the work units; units that run at the same time on one
+//   XCD (workgroup id mod 8) are given neighbouring tiles so they share A and
+//   B lines in that XCD's L2.
+// * Stream-K for shapes with fewer tiles than CUs: a tile's K range is cut
+//   into S parts (decode tiles) or all (tile, slice) iterations are divided
+//   into equal runs (large tiles).  A run that covers part of a tile writes
+//   an fp32 partial; the last one to arrive (arrival counter) sums the
+//   partials in K order - a fixed order, so results are bit-identical run to
+//   run - and stores bf16.  No workgroup ever waits for another.  The pages
+//   fill idle SMs with unaligned block widths (project introduction,
+//   Optimisations); dividing K does that here.
+// * Layouts: dense, grouped-contiguous (an expert id per row), grouped-masked
+//   (valid rows per expert, read on the device) and K-grouped (an expert's
+//   tokens are a K range; per-row scales on both operands).
+// * Scale formats: fp32 (promotion on the VALU), power-of-two UE8M0 (applied
+//   inside v_mfma_scale_f32_16x16x128_f8f6f4, no VALU promotion) and fp32 row
+//   scales on B (K-grouped).  The epilogue can also quantise the bf16 output
+//   per 1x128 tile for the next layer.
 
 #include <stdlib.h>
 #include <string.h>
