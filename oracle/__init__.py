@@ -15,6 +15,8 @@ ue8m0     the same quantisers with power-of-two (UE8M0) scales: the smallest
 gemm      dense NT, grouped-contiguous and grouped-masked reference GEMMs that
           accumulate each 128-wide K slice exactly in fp64, scale it by
           sa*sb and promote it; plus an exact-rational brute force.
+majors    the dense GEMM with the NN, TN and TT operand majors and the 1x128
+          quantiser of an M-major (column-stored) activation matrix.
 kgrouped  the K-axis grouped GEMM (groups of 128-aligned K ranges, 1x128
           scales along K on both operands) and its exact brute force.
 bf16      bit-level helpers for bf16 storage and RNE rounding to bf16.
@@ -39,4 +41,4 @@ tests/test_oracle_*.py against things other than itself (torch's CPU e4m3
 cast, exact rational brute force, closed forms, invariants).
 """
 
-from . import bf16, e4m3, gemm, kgrouped, quant, ue8m0  # noqa: F401
+from . import bf16, e4m3, gemm, kgrouped, majors, quant, ue8m0  # noqa: F401
