@@ -58,8 +58,8 @@ PAGES_TFLOPS = _load_pages_tflops()
 
 def pages_key(wl):
     """The pages' table row of a workload, or None (random masked counts are not a row)."""
-    if wl.layout == "masked" and not wl.all_valid:
-        return None
+    if (wl.layout == "masked" and not wl.all_valid) or wl.extra.get("majors", "nt") != "nt":
+        return None  # the tables hold NT GEMMs only
     key = (wl.layout, wl.groups, wl.m, wl.n, wl.k)
     return key if key in PAGES_TFLOPS else None
 
@@ -133,12 +133,19 @@ class Prepared:
         kg = wl.layout == "k_grouped"
         if kg and ue:
             raise SystemExit("the K-grouped GEMM takes fp32 scales only")
+        # Operand majors of a dense workload: "nt" (default), "nn", "tn", "tt".
+        self.majors = wl.extra.get("majors", "nt")
+        a_mn, b_mn = self.majors[0] == "t", self.majors[1] == "n"
+        if self.majors != "nt" and ue:
+            raise SystemExit("the NN / TN / TT GEMMs take fp32 scales only")
         if wl.layout in ("dense", "k_grouped"):
             self.m_rows, a_shape = wl.m, (wl.m, k)
         elif wl.layout == "contiguous":
             self.m_rows, a_shape = g * wl.m, (g * wl.m, k)
         else:
             self.m_rows, a_shape = wl.m, (g, wl.m, k)
+        if a_mn:
+            a_shape = (k, wl.m)  # stored [K][M]
         xa = synth.bf16_normal(a_shape, wl.seed_a)
         self.x = torch.from_numpy(xa.view(np.int16)).to(dev)
         self.a = torch.empty(a_shape, dtype=torch.uint8, device=dev)
@@ -155,6 +162,8 @@ class Prepared:
             sfb = torch.empty(((g,) if wl.layout != "dense" else ()) + sfb_shape, dtype=sf_dtype, device=dev)
             (dg.dg_quant_128x128_ue8m0 if ue else dg.dg_quant_128x128)(xb, qb, sfb)
         del xb
+        if b_mn:
+            qb = qb.t().contiguous()  # N-major storage of the same codes (set-up, not timed)
         set_bytes = qb.numel() + sfb.numel() * sfb.element_size()
         copies = max(1, math.ceil(2 * MALL_BYTES / set_bytes)) if set_bytes < 2 * MALL_BYTES else 1
         copies = min(copies, 64)
@@ -189,11 +198,12 @@ class Prepared:
         # One kernel instance per (tile variant, layout, stream-K or not): the
         # unit rocprofv3 reports durations for.
         fields = dict(kv.split("=") for kv in self.config.split())
+        lay = wl.layout if self.majors == "nt" else f"{wl.layout}_{self.majors}"
         self.kernel_key = (f"gemm_kernel variant={fields['variant']} bm={fields['bm']} bn={fields['bn']} "
-                           f"layout={wl.layout} stream_k={fields['stream_k']} scales={scales}")
+                           f"layout={lay} stream_k={fields['stream_k']} scales={scales}")
         sfx = "_ue8m0" if ue else ""
-        self._quant_a = getattr(dg, "dg_quant_1x128" + sfx)
-        self._gemm = getattr(dg, {"dense": "dg_fp8_gemm_nt", "contiguous": "dg_grouped_contiguous",
+        self._quant_a = getattr(dg, "dg_quant_1x128_mn" if a_mn else "dg_quant_1x128" + sfx)
+        self._gemm = getattr(dg, {"dense": f"dg_fp8_gemm_{self.majors}", "contiguous": "dg_grouped_contiguous",
                                   "masked": "dg_grouped_masked", "k_grouped": "dg_k_grouped_nt"}[wl.layout] + sfx)
 
     def quant(self, dg):

@@ -206,6 +206,39 @@ int dg_k_grouped_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const 
                     const int32_t* k_offsets, int num_groups, int m, int n, int k, int64_t ld_sfa,
                     int64_t ld_sfb, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Dense GEMM with the other operand majors: NN, TN and TT beside NT ("DeepGEMM:
+ * efficient BLAS kernel library on GPU", yfxerp.com, section 3.1, which lists
+ * the four layouts without defining them).  Reading taken here: the letters
+ * name the operations in D = op(A) * op(B) on row-major storage, NT being
+ * D = A * B^T with a [m][k] and b [n][k].  So
+ *   NN: a [m][lda] (K-major),  b [k][ldb] (N-major: B(n, kk) at b + kk*ldb + n)
+ *   TN: a [k][lda] (M-major: A(r, kk) at a + kk*lda + r), b [k][ldb] (N-major)
+ *   TT: a [k][lda] (M-major),  b [n][ldb] (K-major)
+ * and in every case D[r][c] = bf16( sum_kb P_kb[r][c] * (sfa[kb][r] * sfb[c/128][kb]) )
+ * with the scales in the NT layouts: sfa [k/128][ld_sfa] (one scale per row
+ * of the logical A and 128-deep K slice), sfb [ceil(n/128)][k/128] (one per
+ * 128x128 block of the logical B).  The codes are the same bytes as for NT,
+ * stored transposed: a 1x128 tile along K of an M-major A is a column
+ * segment of 128 rows (dg_quant_1x128_mn produces it); a 128x128 weight block
+ * is a block either way, so an N-major B can take the codes of
+ * dg_quant_128x128 applied to its [k][n] storage with that call's scale
+ * matrix transposed (when n % 128 == 0).
+ * Rules as for dg_fp8_gemm_nt, except for an M-major A: m % 16 == 0,
+ * lda >= m, lda % 16 == 0, k * lda < 2^32; for an N-major B: n % 16 == 0,
+ * ldb >= n, ldb % 16 == 0, k * ldb < 2^32.  Workspace as for dg_fp8_gemm_nt
+ * (the same tile choice and work division).
+ */
+int dg_fp8_gemm_nn(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
+                   int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream);
+int dg_fp8_gemm_tn(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
+                   int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream);
+int dg_fp8_gemm_tt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
+                   int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ----------------------------------------------------------- quantisers -- */
 
 /*
@@ -225,6 +258,19 @@ int dg_k_grouped_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const 
  */
 int dg_quant_1x128(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
                    int64_t ld_sf, int num_groups, void* stream);
+
+/*
+ * The same activation quantiser for an M-major matrix (the A operand of the
+ * TN and TT GEMMs above): x is stored [rows][cols] = [K][M], and the 1x128
+ * tiles run along K, i.e. tile (kb, c) is the column segment
+ * x[128 kb .. 128 kb + 127][c].  The result equals dg_quant_1x128 applied to
+ * x^T (rows and cols swapped) with its codes stored transposed:
+ *   q  [rows][cols] e4m3 (the layout of x)
+ *   sf [rows/128][ld_sf] fp32; entries for columns in [cols, ld_sf) are 0.
+ * rows % 128 == 0, cols % 8 == 0, ld_sf >= cols and a multiple of 4.
+ */
+int dg_quant_1x128_mn(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols, int64_t ld_sf,
+                      void* stream);
 
 /*
  * Weight quantiser, one fp32 scale per 128x128 block (same sources and the

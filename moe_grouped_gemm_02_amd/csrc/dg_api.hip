@@ -112,6 +112,8 @@ int run_gemm(int layout, dg::GemmParams& p, int rows, int groups, void* ws, size
   const dg::GemmConfig cfg = dg::choose_config(layout, rows, p.n, p.k, groups, cus, expected_m, qout);
   if (layout == dg::kKGrouped && !dg::kgrouped_variant_built(cfg.variant))
     return fail(DG_ERR_UNSUPPORTED_SHAPE, "tile variant %d is not built for the K-grouped layout", cfg.variant);
+  if (p.majors && !dg::majors_variant_built(cfg.variant))
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "tile variant %d is not built for MN-major operands", cfg.variant);
   if (p.sf_ue8m0 && !dg::ue8m0_variant_built(cfg.variant))
     return fail(DG_ERR_UNSUPPORTED_SHAPE, "tile variant %d is not built for UE8M0 scales", cfg.variant);
   if (qout && !dg::variant_quantises_output(cfg.variant))
@@ -182,6 +184,40 @@ int gemm_nt_impl(const uint8_t* a, const void* sfa, const uint8_t* b, const void
   set_qout(p, qo, m, n);
   p.m = m; p.n = n; p.k = k; p.num_groups = 1;
   p.lda = lda; p.ldb = ldb; p.ldd = ldd; p.ld_sfa = ld_sfa;
+  return run_gemm(dg::kDense, p, m, 1, workspace, workspace_bytes, stream);
+}
+
+// Dense GEMM with MN-major operands.  majors bit 0: A is stored M-major as
+// [K][lda] (lda >= m, m % 16 == 0); bit 1: B is stored N-major as [K][ldb]
+// (ldb >= n, n % 16 == 0).  Scales keep the K-major (NT) layouts.
+int gemm_majors_impl(int majors, const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                     uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd, int64_t ld_sfa,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  const bool at = (majors & 1) != 0, bt = (majors & 2) != 0;
+  // The common checks see a K-major leading dimension for a transposed
+  // operand; its own rules follow.
+  int st = check_gemm_common(a, sfa, b, sfb, d, m, n, k, at ? k : lda, bt ? k : ldb, ldd, ld_sfa);
+  if (st != DG_SUCCESS) return st;
+  const int64_t lim = (int64_t)1 << 32;
+  if (at) {
+    if (m % 16) return fail(DG_ERR_UNSUPPORTED_SHAPE, "m=%d is not a multiple of 16 (M-major A)", m);
+    if (lda < m) return fail(DG_ERR_INVALID_VALUE, "lda smaller than m (M-major A)");
+    if (lda % 16) return fail(DG_ERR_MISALIGNED, "lda must be a multiple of 16 bytes");
+    if ((int64_t)k * lda >= lim) return fail(DG_ERR_UNSUPPORTED_SHAPE, "operand of 4 GiB or more");
+  }
+  if (bt) {
+    if (n % 16) return fail(DG_ERR_UNSUPPORTED_SHAPE, "n=%d is not a multiple of 16 (N-major B)", n);
+    if (ldb < n) return fail(DG_ERR_INVALID_VALUE, "ldb smaller than n (N-major B)");
+    if (ldb % 16) return fail(DG_ERR_MISALIGNED, "ldb must be a multiple of 16 bytes");
+    if ((int64_t)k * ldb >= lim) return fail(DG_ERR_UNSUPPORTED_SHAPE, "operand of 4 GiB or more");
+  }
+  if (m == 0 || n == 0) return ok();
+  dg::GemmParams p{};
+  p.a = a; p.b = b; p.d = d;
+  set_scales(p, sfa, sfb, n, k, false);
+  p.m = m; p.n = n; p.k = k; p.num_groups = 1;
+  p.lda = lda; p.ldb = ldb; p.ldd = ldd; p.ld_sfa = ld_sfa;
+  p.majors = majors;
   return run_gemm(dg::kDense, p, m, 1, workspace, workspace_bytes, stream);
 }
 
@@ -272,6 +308,22 @@ int quant_1x128_impl(const uint16_t* x, uint8_t* q, void* sf, int rows, int cols
   return ok();
 }
 
+int quant_1x128_mn_impl(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols, int64_t ld_sf,
+                        void* stream) {
+  if (rows < 0 || cols < 0) return fail(DG_ERR_INVALID_VALUE, "bad sizes (rows=%d cols=%d)", rows, cols);
+  if (rows % 128) return fail(DG_ERR_UNSUPPORTED_SHAPE, "rows=%d (K) is not a multiple of 128", rows);
+  if (cols % 8) return fail(DG_ERR_UNSUPPORTED_SHAPE, "cols=%d is not a multiple of 8", cols);
+  if (ld_sf < cols) return fail(DG_ERR_INVALID_VALUE, "ld_sf smaller than cols");
+  if (ld_sf % 4) return fail(DG_ERR_MISALIGNED, "ld_sf must be a multiple of 4");
+  if (rows / 128 > 65535) return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many K blocks");
+  if (!x || !q || !sf) return fail(DG_ERR_INVALID_VALUE, "null pointer argument");
+  if (!aligned16(x) || !aligned16(q) || !aligned16(sf)) return fail(DG_ERR_MISALIGNED, "x, q and sf must be 16-byte aligned");
+  if (rows == 0 || ld_sf == 0) return ok();
+  const hipError_t e = dg::launch_quant_1x128_mn(x, q, sf, rows, cols, ld_sf, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(DG_ERR_HIP, "quant_1x128_mn launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int quant_128x128_impl(const uint16_t* w, uint8_t* q, void* sf, int rows, int cols, int num_groups,
                        bool pow2, void* stream) {
   if (rows < 0 || cols < 0 || num_groups < 1) return fail(DG_ERR_INVALID_VALUE, "bad sizes (rows=%d cols=%d groups=%d)", rows, cols, num_groups);
@@ -295,6 +347,24 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
                    int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream) {
   return gemm_nt_impl(a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, workspace, workspace_bytes,
                       stream, false);
+}
+
+int dg_fp8_gemm_nn(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
+                   int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_majors_impl(2, a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, workspace, workspace_bytes, stream);
+}
+
+int dg_fp8_gemm_tn(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
+                   int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_majors_impl(3, a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, workspace, workspace_bytes, stream);
+}
+
+int dg_fp8_gemm_tt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                   uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
+                   int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_majors_impl(1, a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, workspace, workspace_bytes, stream);
 }
 
 int dg_fp8_gemm_nt_ue8m0(const uint8_t* a, const uint8_t* sfa, const uint8_t* b,
@@ -376,6 +446,11 @@ int dg_k_grouped_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const 
 int dg_quant_1x128(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
                    int64_t ld_sf, int num_groups, void* stream) {
   return quant_1x128_impl(x, q, sf, rows, cols, ld_sf, num_groups, false, stream);
+}
+
+int dg_quant_1x128_mn(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols, int64_t ld_sf,
+                      void* stream) {
+  return quant_1x128_mn_impl(x, q, sf, rows, cols, ld_sf, stream);
 }
 
 int dg_quant_1x128_ue8m0(const uint16_t* x, uint8_t* q, uint8_t* sf, int rows, int cols,

@@ -38,6 +38,11 @@
 // * Layouts: dense, grouped-contiguous (an expert id per row), grouped-masked
 //   (valid rows per expert, read on the device) and K-grouped (an expert's
 //   tokens are a K range; per-row scales on both operands).
+// * Operand majors (dense layout, fp32 scales): A may also be stored M-major
+//   ([K][lda]) and B N-major ([K][ldb]), the TN / NN / TT forms of D = A B^T
+//   beside NT.  Such a tile is staged as [128][BM] (K rows of BM bytes) and
+//   its fragments are read with ds_read_b64_tr_b8, gfx950's transposing LDS
+//   load, which hands each lane the 8 K values of its own row.
 // * Scale formats: fp32 (promotion on the VALU), power-of-two UE8M0 (applied
 //   inside v_mfma_scale_f32_16x16x128_f8f6f4, no VALU promotion) and fp32 row
 //   scales on B (K-grouped).  The epilogue can also quantise the bf16 output
@@ -107,6 +112,56 @@ __device__ __forceinline__ v8i make_v8i(uint4 lo, uint4 hi) {
   v8i r;
   r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
   r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+  return r;
+}
+
+// MN-major operand tiles.  A K slice of an M-major A (or N-major B) tile is
+// held in LDS as 128 K rows of L = BM (BN) bytes; the 16-byte chunk c of K
+// row k sits at position c ^ mn_swizzle<L>(k), so that the 8 K rows read
+// together by one transposing load (same chunk, 8 consecutive rows) fall in
+// 8 distinct 16-byte bank groups.
+template <int L>
+__device__ __forceinline__ int mn_swizzle(int k) {
+  static_assert(L % 128 == 0 || L == 64, "MN-major tiles are 64 or a multiple of 128 bytes wide");
+  return L >= 128 ? (k & 7) : ((k >> 1) & 3);
+}
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+
+// The MFMA operand of the 16 rows (MN indices) col .. col + 15 of an MN-major
+// tile: lane l gets row col + l % 16, K bytes 32 (l / 16) .. + 31, the same
+// layout as a K-major fragment.  ds_read_b64_tr_b8 works on groups of 16
+// lanes: lane r of the group names an 8-byte row R_r, and lane i receives
+// the bytes R_{2j + i/8}[i % 8], j = 0..7 (measured on gfx950).  So lane r
+// points at K row kbase + r / 2, MN bytes col + 8 (r % 2) .. + 7, and lane i
+// then holds MN index col + i at K rows kbase .. kbase + 7.  Four loads
+// (kbase = 32 (l / 16) + 8 t, immediate offsets 8 t L) give the 32 bytes.
+//
+// For every K row this lane names, k = 32 kg + 8 t + fr / 2, so its swizzle
+// term x = mn_swizzle(fr / 2) is fixed per lane and sits in address bits
+// 4..6 of `lane_off` (the tile base is 1 KB aligned and K rows are a
+// multiple of 128 bytes, or 64 bytes with a 2-bit term).  The chunk's low
+// bits then enter by XOR, col's higher bits by addition, so a fragment
+// costs one add and one xor and no per-fragment register stays live.
+template <int L>
+__device__ __forceinline__ uint32_t mn_lane_off(int fr, int kg) {
+  return (uint32_t)((32 * kg + (fr >> 1)) * L + 16 * mn_swizzle<L>(fr >> 1) + 8 * (fr & 1));
+}
+
+template <int L>
+__device__ __forceinline__ v8i ld_mn_frag(uint32_t tile_lds, uint32_t lane_off, int col) {
+  constexpr int kLow = L >= 128 ? 7 : 3;  // chunk bits taken by the swizzle
+  const int c = col >> 4;
+  const uint32_t addr = (tile_lds + lane_off + 16u * (uint32_t)(c & ~kLow)) ^ (16u * (uint32_t)(c & kLow));
+  lds_v2i* p = (lds_v2i*)(uintptr_t)addr;
+  v8i r;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(p + t * L);  // + 8 t L bytes
+    r[2 * t] = v.x;
+    r[2 * t + 1] = v.y;
+  }
   return r;
 }
 
@@ -210,8 +265,13 @@ __device__ __forceinline__ const float* scale_ptr(const float* base, int64_t off
 
 // SF: kScaleF32 (fp32 scales, promoted on the VALU) or kScaleUE8M0 (power-of-
 // two exponents applied inside the block-scaled MFMA, see below).
-template <class T, int LAYOUT, bool SK, int SF>
+// MAJ: operand majors, bit 0 = A stored M-major [K][lda], bit 1 = B stored
+// N-major [K][ldb] (dense layout, fp32 scales).
+constexpr int kAMajorMN = 1, kBMajorMN = 2;
+template <class T, int LAYOUT, bool SK, int SF, int MAJ = 0>
 __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedule s) {
+  static_assert(MAJ == 0 || (LAYOUT == kDense && SF == kScaleF32), "MN-major operands: dense layout, fp32 scales");
+  constexpr bool kAT = (MAJ & kAMajorMN) != 0, kBT = (MAJ & kBMajorMN) != 0;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::STAGES * T::kStageBytes];
   __shared__ int last_flag;
 
@@ -405,16 +465,33 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
         if constexpr (j < T::kAJ) {
           const int instr = j * T::kWaves + wave;
           const int q = instr * 64 + lane;
-          const int r = q >> 3, c = (q & 7) ^ (r & 7);
-          const int gr = min(m0 + r, rows_valid - 1);
-          dma16(stage_lds + instr * 1024, A, (uint32_t)gr * (uint32_t)p.lda + kb * 128 + c * 16);
+          if constexpr (kAT) {
+            // K row kr of the slice, chunk position cp; the chunk holds rows
+            // m .. m + 15 (M % 16 == 0, so a chunk is all valid or all past
+            // the end, and those are clamped onto the last valid chunk).
+            constexpr int C = T::BM / 16;
+            const int kr = q / C, c = (q % C) ^ mn_swizzle<T::BM>(q / C);
+            const int gm = min(m0 + 16 * c, p.m - 16);
+            dma16(stage_lds + instr * 1024, A, (uint32_t)(kb * 128 + kr) * (uint32_t)p.lda + gm);
+          } else {
+            const int r = q >> 3, c = (q & 7) ^ (r & 7);
+            const int gr = min(m0 + r, rows_valid - 1);
+            dma16(stage_lds + instr * 1024, A, (uint32_t)gr * (uint32_t)p.lda + kb * 128 + c * 16);
+          }
         } else if constexpr (j < T::kLPW) {
           constexpr int jb = j - T::kAJ;
           const int instr = (T::kAJ + jb) * T::kWaves + wave;
           const int q = (jb * T::kWaves + wave) * 64 + lane;
-          const int r = q >> 3, c = (q & 7) ^ (r & 7);
-          const int gn = min(n0 + r, p.n - 1);
-          dma16(stage_lds + instr * 1024, B, (uint32_t)gn * (uint32_t)p.ldb + kb * 128 + c * 16);
+          if constexpr (kBT) {
+            constexpr int C = T::BN / 16;
+            const int kr = q / C, c = (q % C) ^ mn_swizzle<T::BN>(q / C);
+            const int gn = min(n0 + 16 * c, p.n - 16);
+            dma16(stage_lds + instr * 1024, B, (uint32_t)(kb * 128 + kr) * (uint32_t)p.ldb + gn);
+          } else {
+            const int r = q >> 3, c = (q & 7) ^ (r & 7);
+            const int gn = min(n0 + r, p.n - 1);
+            dma16(stage_lds + instr * 1024, B, (uint32_t)gn * (uint32_t)p.ldb + kb * 128 + c * 16);
+          }
         } else {
           if constexpr (SF == kScaleUE8M0) {
             // Exponent bytes, MN-major for both operands (four to a dword).
@@ -670,18 +747,26 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
             v8i bfrag[T::FN];
   #pragma unroll
             for (int j = 0; j < T::FN; ++j) {
-              const uint8_t* rowp = st + T::kBOff + (wn * T::TN + j * 16 + fr) * 128;
-              bfrag[j] = make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
-                                  *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
+              if constexpr (kBT) {
+                bfrag[j] = ld_mn_frag<T::BN>(lds_addr(st) + T::kBOff, mn_lane_off<T::BN>(fr, kg), wn * T::TN + j * 16);
+              } else {
+                const uint8_t* rowp = st + T::kBOff + (wn * T::TN + j * 16 + fr) * 128;
+                bfrag[j] = make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
+                                    *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
+              }
             }
             // Software pipeline over the fragment rows: the MFMAs of row i+1 are
             // issued into a second set of result registers before the promotion
             // FMAs of row i, so the matrix core and the VALU overlap instead of
             // each FMA waiting on the MFMA just issued.
             auto load_a = [&](int i) {
-              const uint8_t* rowp = st + (wm * T::TM + i * 16 + fr) * 128;
-              return make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
-                              *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
+              if constexpr (kAT) {
+                return ld_mn_frag<T::BM>(lds_addr(st), mn_lane_off<T::BM>(fr, kg), wm * T::TM + i * 16);
+              } else {
+                const uint8_t* rowp = st + (wm * T::TM + i * 16 + fr) * 128;
+                return make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
+                                *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
+              }
             };
             auto load_s = [&](int i) {
               return *reinterpret_cast<const float4*>(st + T::kSOff + (wm * T::TM + i * 16 + 4 * kg) * 4);
@@ -987,6 +1072,26 @@ hipError_t launch_one(const GemmParams& p, const Schedule& s, int grid, hipStrea
   return hipGetLastError();
 }
 
+// Dense GEMM with MN-major operands (p.majors: kAMajorMN | kBMajorMN).
+template <class T, int MAJ>
+hipError_t launch_majors_one(const GemmParams& p, const Schedule& s, int grid, hipStream_t stream) {
+  if (s.stream_k)
+    hipLaunchKernelGGL((gemm_kernel<T, kDense, true, kScaleF32, MAJ>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
+  else
+    hipLaunchKernelGGL((gemm_kernel<T, kDense, false, kScaleF32, MAJ>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
+  return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_majors(const GemmParams& p, const Schedule& s, int grid, hipStream_t stream) {
+  switch (p.majors) {
+    case kAMajorMN: return launch_majors_one<T, kAMajorMN>(p, s, grid, stream);
+    case kBMajorMN: return launch_majors_one<T, kBMajorMN>(p, s, grid, stream);
+    case kAMajorMN | kBMajorMN: return launch_majors_one<T, kAMajorMN | kBMajorMN>(p, s, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <class T, int SF>
 hipError_t launch_layout(int layout, const GemmParams& p, const Schedule& s, int grid, hipStream_t stream) {
   switch (layout) {
@@ -1163,6 +1268,16 @@ hipError_t launch_gemm(int layout, const GemmParams& p0, const GemmConfig& cfg,
       case 4: return launch_kgrouped<TileS64>(p, s, cfg.grid, stream);
       case 5: return launch_kgrouped<TileW128>(p, s, cfg.grid, stream);
       case 6: return launch_kgrouped<TileP128w8>(p, s, cfg.grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (p.majors) {  // MN-major operands: dense, fp32 scales, the dense heuristic's tiles
+    if (layout != kDense || p.sf_ue8m0) return hipErrorInvalidValue;
+    switch (cfg.variant) {
+      case 0: return launch_majors<TileP256>(p, s, cfg.grid, stream);
+      case 4: return launch_majors<TileS64>(p, s, cfg.grid, stream);
+      case 5: return launch_majors<TileW128>(p, s, cfg.grid, stream);
+      case 6: return launch_majors<TileP128w8>(p, s, cfg.grid, stream);
       default: return hipErrorInvalidValue;
     }
   }

@@ -100,6 +100,73 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __rest
   }
 }
 
+// 1x128 activation tiles of an M-major matrix: x is stored [K][M] (the K
+// values of logical row m are a column), and tile (kb, m) is the column
+// segment x[128 kb .. 128 kb + 127][m].  The codes keep the [K][M] layout;
+// the scales are [K/128][ld_sf] as for the row form, so this is
+// quant_1x128 of x^T with its codes stored transposed.  A wave covers 64
+// columns and 128 rows: lane l owns columns 8 (l % 8) .. + 7 of the wave's
+// 64 and rows 16 (l / 8) .. + 15, held in registers between the amax and the
+// encode; the 8 lanes of a column group combine their amax with shuffles.
+// Block (x, y): columns [256 x, 256 x + 256), K block y; cols % 8 == 0.
+__global__ __launch_bounds__(256) void quant_1x128_mn_kernel(const uint16_t* __restrict__ x,
+                                                             uint8_t* __restrict__ q,
+                                                             float* __restrict__ sf, int rows,
+                                                             int cols, int64_t ld_sf) {
+  const int lane = threadIdx.x & 63;
+  const int col = blockIdx.x * 256 + (threadIdx.x >> 6) * 64 + (lane & 7) * 8;
+  const int kb = blockIdx.y;
+  const int r0 = kb * kBlockK + (lane >> 3) * 16;
+  if (col < cols) {
+    uint4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const uint4*>(x + (int64_t)(r0 + i) * cols + col);
+    float amax[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) amax[c] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        amax[2 * h] = fmaxf(amax[2 * h], fabsf(bf16_bits_to_f32(w[h] & 0xFFFFu)));
+        amax[2 * h + 1] = fmaxf(amax[2 * h + 1], fabsf(bf16_bits_to_f32(w[h] >> 16)));
+      }
+    }
+    // The 8 lanes l, l + 8, ..., l + 56 hold the 8 row groups of a column group.
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int off = 8; off <= 32; off <<= 1) amax[c] = fmaxf(amax[c], __shfl_xor(amax[c], off, 64));
+    double rcp[8];
+    float s[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      s[c] = amax[c] / 448.0f;
+      rcp[c] = tile_reciprocal(s[c]);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+      const uint32_t lo = e4m3_x4(quotient(w[0] & 0xFFFFu, rcp[0]), quotient(w[0] >> 16, rcp[1]),
+                                  quotient(w[1] & 0xFFFFu, rcp[2]), quotient(w[1] >> 16, rcp[3]));
+      const uint32_t hi = e4m3_x4(quotient(w[2] & 0xFFFFu, rcp[4]), quotient(w[2] >> 16, rcp[5]),
+                                  quotient(w[3] & 0xFFFFu, rcp[6]), quotient(w[3] >> 16, rcp[7]));
+      *reinterpret_cast<uint2*>(q + (int64_t)(r0 + i) * cols + col) = make_uint2(lo, hi);
+    }
+    if ((lane >> 3) == 0) {
+      float* out = sf + (int64_t)kb * ld_sf + col;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) out[c] = s[c];
+    }
+  }
+  // Padding entries of the scale matrix (columns in [cols, ld_sf)) are zero.
+  const int pad = (int)(ld_sf - cols);
+  if (pad > 0 && blockIdx.x == 0 && (int)threadIdx.x < pad) {
+    for (int i = threadIdx.x; i < pad; i += 256) sf[(int64_t)kb * ld_sf + cols + i] = 0.0f;
+  }
+}
+
 // One 128x128 block per workgroup of 256 threads: 2048 16-byte chunks, 8 per
 // thread, held in registers between the amax reduction and the encode.
 // POW2: UE8M0 exponents in an MN-major [G][K/128][ld_n] byte matrix,
@@ -178,6 +245,13 @@ hipError_t launch_quant_1x128(const uint16_t* x, uint8_t* q, void* sf, int rows,
     hipLaunchKernelGGL(quant_1x128_kernel<true>, grid, dim3(256), 0, stream, x, q, sf, rows, cols, ld_sf, groups);
   else
     hipLaunchKernelGGL(quant_1x128_kernel<false>, grid, dim3(256), 0, stream, x, q, sf, rows, cols, ld_sf, groups);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_1x128_mn(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
+                                 int64_t ld_sf, hipStream_t stream) {
+  const dim3 grid((cols + 255) / 256, rows / kBlockK);
+  hipLaunchKernelGGL(quant_1x128_mn_kernel, grid, dim3(256), 0, stream, x, q, sf, rows, cols, ld_sf);
   return hipGetLastError();
 }
 

@@ -129,7 +129,20 @@ def extra_workloads():
     return [Workload("k_grouped_g8_m7168_n2048_k8192", "k_grouped", 7168, 2048, 8192, groups=8, number=6,
                      extra={"tokens": [1024, 640, 1536, 0, 1152, 2048, 896, 896]}),
             Workload("k_grouped_g8_m7168_n2048_k8192_equal", "k_grouped", 7168, 2048, 8192, groups=8, number=6,
-                     extra={"tokens": [1024] * 8})]
+                     extra={"tokens": [1024] * 8})] + majors_workloads()
+
+
+def majors_workloads():
+    """The dense prefill (4096 x 4096 x 7168) and decode (128 x 7168 x 16384)
+    shapes in the NN, TN and TT operand majors (A stored [K][M] for T, B
+    stored [K][N] for the second letter N).  Same seeds as the NT shapes."""
+    out = []
+    for mj in ("nn", "tn", "tt"):
+        out.append(Workload(f"dense_{mj}_m4096_n4096_k7168", "dense", 4096, 4096, 7168, number=3,
+                            extra={"majors": mj}))
+        out.append(Workload(f"dense_{mj}_m128_n7168_k16384", "dense", 128, 7168, 16384, number=2,
+                            extra={"majors": mj}))
+    return out
 
 
 def k_group_offsets(wl: "Workload") -> np.ndarray:
