@@ -111,13 +111,14 @@ def test_num_cus_override():
 
 def test_stream_k_workspace_size():
     # Decode-sized tiles: S equal K parts per tile, one workgroup per part (grid
-    # rounded up to a multiple of 8), two fp32 partial slots per part plus one
-    # arrival counter per tile.
+    # rounded up to a multiple of 8; up to two per CU for the 64x64 tiles, which
+    # share a CU), two fp32 partial slots per part plus one arrival counter per
+    # tile.
     for n, k in [(2112, 7168), (7168, 16384), (4096, 7168)]:
         fields = dict(kv.split("=") for kv in dg.dg_describe_config(dg.LAYOUT_DENSE, 128, n, k, 1, 256).split())
         grid, bm, bn, tiles, parts = (int(fields[x]) for x in ("grid", "bm", "bn", "tiles", "sk_split"))
         assert int(fields["stream_k"]) == 1 and parts >= 2
-        assert grid == -(-tiles * parts // 8) * 8 <= 256
+        assert grid == -(-tiles * parts // 8) * 8 <= 256 * (2 if bm * bn == 64 * 64 else 1)
         assert int(fields["workspace"]) == 2 * tiles * parts * bm * bn * 4 + tiles * 4
     # Large tiles that fill under 70% of the CUs, long K: equal runs over all CUs.
     fields = dict(kv.split("=") for kv in dg.dg_describe_config(dg.LAYOUT_DENSE, 4096, 2112, 7168, 1, 256).split())
