@@ -170,3 +170,48 @@ def test_qout_configuration_uses_whole_column_blocks():
         assert dg.dg_get_workspace_size(64, 2048, 7168, 1) >= max(int(plain["workspace"]), int(fused["workspace"]))
     finally:
         dg.dg_set_num_cus(0)
+
+
+def _gemm_majors(fn, **kw):
+    args = dict(a=FAKE, sfa=FAKE, b=FAKE, sfb=FAKE, d=FAKE, m=64, n=2112, k=7168, lda=64,
+                ldb=2112, ldd=2112, ld_sfa=64, ws=None, ws_bytes=0, stream=None)
+    args.update(kw)
+    ptrs = ("a", "sfa", "b", "sfb", "d", "ws", "stream")
+    order = ("a", "sfa", "b", "sfb", "d", "m", "n", "k", "lda", "ldb", "ldd", "ld_sfa", "ws", "ws_bytes", "stream")
+    return getattr(dg.raw(), fn)(*[ctypes.c_void_p(args[x]) if x in ptrs else args[x] for x in order])
+
+
+@pytest.mark.parametrize("fn,kw,status", [
+    ("dg_fp8_gemm_tn", dict(m=40, lda=48, ld_sfa=40), -2),    # M-major A: m % 16
+    ("dg_fp8_gemm_tn", dict(lda=48), -1),                      # lda < m
+    ("dg_fp8_gemm_tn", dict(lda=72), -3),                      # lda % 16
+    ("dg_fp8_gemm_tn", dict(n=2104, ldb=2112, ldd=2104), -2),  # N-major B: n % 16
+    ("dg_fp8_gemm_tn", dict(ldb=2096), -1),                    # ldb < n
+    ("dg_fp8_gemm_tn", dict(ldb=2120), -3),                    # ldb % 16
+    ("dg_fp8_gemm_tt", dict(ldb=7000), -1),                    # K-major B keeps its own rules
+    ("dg_fp8_gemm_nn", dict(lda=7000), -1),                    # K-major A keeps its own rules
+    ("dg_fp8_gemm_nn", dict(k=7000), -2),                      # k % 128
+])
+def test_operand_major_argument_errors(fn, kw, status):
+    if fn == "dg_fp8_gemm_tt":
+        kw = dict(dict(ldb=7168), **kw)
+    if fn == "dg_fp8_gemm_nn":
+        kw = dict(dict(lda=7168), **kw)
+    assert _gemm_majors(fn, **kw) == status
+    assert dg.dg_get_last_error_string() != ""
+
+
+def test_operand_major_zero_sized_is_a_noop():
+    assert _gemm_majors("dg_fp8_gemm_tn", m=0, lda=16, ld_sfa=4) == 0
+    assert _gemm_majors("dg_fp8_gemm_tn", n=0, ldb=16, ldd=0) == 0
+
+
+def test_column_quantiser_argument_errors():
+    lib = dg.raw()
+    P = ctypes.c_void_p
+    assert lib.dg_quant_1x128_mn(P(FAKE), P(FAKE), P(FAKE), 100, 64, 64, None) == -2   # rows (K) % 128
+    assert lib.dg_quant_1x128_mn(P(FAKE), P(FAKE), P(FAKE), 128, 60, 60, None) == -2   # cols % 8
+    assert lib.dg_quant_1x128_mn(P(FAKE), P(FAKE), P(FAKE), 128, 64, 60, None) == -1   # ld_sf < cols
+    assert lib.dg_quant_1x128_mn(P(FAKE), P(FAKE), P(FAKE), 128, 64, 66, None) == -3   # ld_sf % 4
+    assert lib.dg_quant_1x128_mn(None, P(FAKE), P(FAKE), 128, 64, 64, None) == -1
+    assert lib.dg_quant_1x128_mn(P(FAKE), P(FAKE), P(FAKE), 0, 64, 64, None) == 0      # nothing to do
