@@ -472,11 +472,15 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
             constexpr int C = T::BM / 16;
             const int kr = q / C, c = (q % C) ^ mn_swizzle<T::BM>(q / C);
             const int gm = min(m0 + 16 * c, p.m - 16);
-            dma16(stage_lds + instr * 1024, A, (uint32_t)(kb * 128 + kr) * (uint32_t)p.lda + gm);
+            // The slice's K rows start at A + 128 kb lda (a uniform base), so
+            // the per-lane offset stays the same from slice to slice.
+            dma16(stage_lds + instr * 1024, A + (size_t)(kb * 128) * (size_t)p.lda,
+                  (uint32_t)kr * (uint32_t)p.lda + (uint32_t)gm);
           } else {
             const int r = q >> 3, c = (q & 7) ^ (r & 7);
             const int gr = min(m0 + r, rows_valid - 1);
-            dma16(stage_lds + instr * 1024, A, (uint32_t)gr * (uint32_t)p.lda + kb * 128 + c * 16);
+            // The slice advances the uniform base; the per-lane offset is fixed.
+            dma16(stage_lds + instr * 1024, A + kb * 128, (uint32_t)gr * (uint32_t)p.lda + c * 16);
           }
         } else if constexpr (j < T::kLPW) {
           constexpr int jb = j - T::kAJ;
@@ -486,11 +490,12 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
             constexpr int C = T::BN / 16;
             const int kr = q / C, c = (q % C) ^ mn_swizzle<T::BN>(q / C);
             const int gn = min(n0 + 16 * c, p.n - 16);
-            dma16(stage_lds + instr * 1024, B, (uint32_t)(kb * 128 + kr) * (uint32_t)p.ldb + gn);
+            dma16(stage_lds + instr * 1024, B + (size_t)(kb * 128) * (size_t)p.ldb,
+                  (uint32_t)kr * (uint32_t)p.ldb + (uint32_t)gn);
           } else {
             const int r = q >> 3, c = (q & 7) ^ (r & 7);
             const int gn = min(n0 + r, p.n - 1);
-            dma16(stage_lds + instr * 1024, B, (uint32_t)gn * (uint32_t)p.ldb + kb * 128 + c * 16);
+            dma16(stage_lds + instr * 1024, B + kb * 128, (uint32_t)gn * (uint32_t)p.ldb + c * 16);
           }
         } else {
           if constexpr (SF == kScaleUE8M0) {
