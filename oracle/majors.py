@@ -18,12 +18,13 @@ sfa [K/128][ld] (one per row of A and 128-deep K slice), sfb
 
 An M-major A is quantised along K, i.e. down its columns: quant_1x128_mn
 takes x stored [K][M] and forms one scale per column segment of 128 rows,
-the 1x128 activation quantiser (quant.py) applied to the logical operand.
+the 1x128 activation quantiser (quant.py) applied to the logical operand;
+quant_1x128_mn_ue8m0 does the same with the power-of-two scales of ue8m0.py.
 """
 
 import numpy as np
 
-from . import bf16, gemm
+from . import bf16, gemm, ue8m0
 from .quant import BLOCK, _codes, _scale, sf_leading_dim
 
 LAYOUTS = ("nt", "nn", "tn", "tt")
@@ -66,4 +67,28 @@ def quant_1x128_mn(x_bits, ld_sf=None):
         s = _scale(np.abs(seg).max(axis=0))     # [M]
         q[kb * BLOCK:(kb + 1) * BLOCK, :] = _codes(seg, s[None, :])
         sf[kb, :cols] = s
+    return q, sf
+
+
+def quant_1x128_mn_ue8m0(x_bits, ld_sf=None):
+    """The column quantiser with UE8M0 scales: (q uint8 [K][M], sf uint8
+    [K/128][ld]) with E per column segment as ue8m0.exponent defines it."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    rows, cols = x_bits.shape
+    if rows % BLOCK:
+        raise ValueError("rows (K) must be a multiple of 128")
+    ld = sf_leading_dim(cols) if ld_sf is None else ld_sf
+    if ld < cols:
+        raise ValueError("scale leading dimension smaller than the columns")
+    x = bf16.to_f32(x_bits)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("NaN/Inf input is outside the contract")
+    q = np.zeros((rows, cols), dtype=np.uint8)
+    sf = np.zeros((rows // BLOCK, ld), dtype=np.uint8)
+    for kb in range(rows // BLOCK):
+        for c in range(cols):
+            seg = x[kb * BLOCK:(kb + 1) * BLOCK, c]
+            e = ue8m0.exponent(float(np.abs(seg).max()))
+            sf[kb, c] = e
+            q[kb * BLOCK:(kb + 1) * BLOCK, c] = ue8m0._codes(seg, e)
     return q, sf

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import e4m3, gemm, majors, quant
+from oracle import e4m3, gemm, majors, quant, ue8m0
 
 LAYOUTS = ["nt", "nn", "tn", "tt"]
 
@@ -138,3 +138,15 @@ def test_column_quantiser_invariants():
             assert q[kb * 128 + r, c] & 0x7F == 0x7E
             err = np.abs(deq[kb * 128:(kb + 1) * 128, c] * sf[kb, c] - seg[:, c])
             assert np.all(err <= 2.0 ** -4 * np.abs(seg[:, c]) + 2.0 ** -10 * sf[kb, c])
+
+
+@pytest.mark.parametrize("k,m,ld", [(256, 40, None), (128, 8, 16)])
+def test_column_ue8m0_quantiser_is_row_quantiser_of_transpose(k, m, ld):
+    x = synth.bf16_normal((k, m), 47 + m)
+    x[0:128, 3] = 0          # all-zero column tile: E = 0
+    x[0:128, 5] = 0x43E0     # 448 everywhere: E = 127
+    q, sf = majors.quant_1x128_mn_ue8m0(x, ld)
+    qt, sft = ue8m0.quant_1x128_ue8m0(np.ascontiguousarray(x.T), ld)
+    assert np.array_equal(q, qt.T)
+    assert np.array_equal(sf, sft)
+    assert sf[0, 3] == 0 and sf[0, 5] == 127
