@@ -136,8 +136,6 @@ class Prepared:
         # Operand majors of a dense workload: "nt" (default), "nn", "tn", "tt".
         self.majors = wl.extra.get("majors", "nt")
         a_mn, b_mn = self.majors[0] == "t", self.majors[1] == "n"
-        if self.majors != "nt" and ue:
-            raise SystemExit("the NN / TN / TT GEMMs take fp32 scales only")
         if wl.layout in ("dense", "k_grouped"):
             self.m_rows, a_shape = wl.m, (wl.m, k)
         elif wl.layout == "contiguous":
@@ -202,7 +200,7 @@ class Prepared:
         self.kernel_key = (f"gemm_kernel variant={fields['variant']} bm={fields['bm']} bn={fields['bn']} "
                            f"layout={lay} stream_k={fields['stream_k']} scales={scales}")
         sfx = "_ue8m0" if ue else ""
-        self._quant_a = getattr(dg, "dg_quant_1x128_mn" if a_mn else "dg_quant_1x128" + sfx)
+        self._quant_a = getattr(dg, ("dg_quant_1x128_mn" if a_mn else "dg_quant_1x128") + sfx)
         self._gemm = getattr(dg, {"dense": f"dg_fp8_gemm_{self.majors}", "contiguous": "dg_grouped_contiguous",
                                   "masked": "dg_grouped_masked", "k_grouped": "dg_k_grouped_nt"}[wl.layout] + sfx)
 

@@ -239,6 +239,24 @@ int dg_fp8_gemm_tt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
                    uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
                    int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The same three with UE8M0 scales, the format the pages give for the
+ * architecture that has the four layouts (same article, section 3.1): sfa
+ * and sfb are exponent bytes in the layouts of dg_fp8_gemm_nt_ue8m0 (sfa
+ * [k/128][ld_sfa], sfb [k/128][dg_get_ue8m0_sfb_leading_dim(n)]), the scales
+ * again belonging to the logical operands; dg_quant_1x128_mn_ue8m0 quantises
+ * an M-major A.  Rules as for the fp32-scale forms.
+ */
+int dg_fp8_gemm_nn_ue8m0(const uint8_t* a, const uint8_t* sfa, const uint8_t* b, const uint8_t* sfb,
+                         uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
+                         int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream);
+int dg_fp8_gemm_tn_ue8m0(const uint8_t* a, const uint8_t* sfa, const uint8_t* b, const uint8_t* sfb,
+                         uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
+                         int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream);
+int dg_fp8_gemm_tt_ue8m0(const uint8_t* a, const uint8_t* sfa, const uint8_t* b, const uint8_t* sfb,
+                         uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
+                         int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ----------------------------------------------------------- quantisers -- */
 
 /*
@@ -301,6 +319,10 @@ int dg_quant_1x128_ue8m0(const uint16_t* x, uint8_t* q, uint8_t* sf, int rows, i
                          int64_t ld_sf, int num_groups, void* stream);
 int dg_quant_128x128_ue8m0(const uint16_t* w, uint8_t* q, uint8_t* sf, int rows, int cols,
                            int num_groups, void* stream);
+/* dg_quant_1x128_mn with UE8M0 scales: sf [rows/128][ld_sf] uint8, columns
+ * [cols, ld_sf) written as 0 (dg_quant_1x128_ue8m0 of x^T, codes transposed). */
+int dg_quant_1x128_mn_ue8m0(const uint16_t* x, uint8_t* q, uint8_t* sf, int rows, int cols, int64_t ld_sf,
+                            void* stream);
 
 /* -------------------------------------------------------------- utilities -- */
 

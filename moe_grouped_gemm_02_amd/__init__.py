@@ -46,6 +46,10 @@ _SIGNATURES = {
     "dg_fp8_gemm_tt": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _L, _L, _P, _S, _P]),
     "dg_quant_1x128": (_I, [_P, _P, _P, _I, _I, _L, _I, _P]),
     "dg_quant_1x128_mn": (_I, [_P, _P, _P, _I, _I, _L, _P]),
+    "dg_quant_1x128_mn_ue8m0": (_I, [_P, _P, _P, _I, _I, _L, _P]),
+    "dg_fp8_gemm_nn_ue8m0": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _L, _L, _P, _S, _P]),
+    "dg_fp8_gemm_tn_ue8m0": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _L, _L, _P, _S, _P]),
+    "dg_fp8_gemm_tt_ue8m0": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _L, _L, _P, _S, _P]),
     "dg_quant_128x128": (_I, [_P, _P, _P, _I, _I, _I, _P]),
     "dg_quant_1x128_ue8m0": (_I, [_P, _P, _P, _I, _I, _L, _I, _P]),
     "dg_quant_128x128_ue8m0": (_I, [_P, _P, _P, _I, _I, _I, _P]),
@@ -209,16 +213,16 @@ def dg_fp8_gemm_nt_ue8m0(a, sfa, b, sfb, d, workspace=None):
     return _gemm_nt("dg_fp8_gemm_nt_ue8m0", a, sfa, b, sfb, d, workspace, True)
 
 
-def _gemm_majors(fn, a_mn, b_mn, a, sfa, b, sfb, d, workspace):
+def _gemm_majors(fn, a_mn, b_mn, a, sfa, b, sfb, d, workspace, ue8m0=False):
     """Dense GEMM whose A is stored [K][M] (a_mn) and/or B [K][N] (b_mn)."""
     _expect(a, "a", _U8, 2), _expect(b, "b", _U8, 2), _expect(d, "d", _BF, 2)
-    _expect(sfa, "sfa", (torch.float32,), 2), _expect(sfb, "sfb", (torch.float32,), 2)
+    _expect(sfa, "sfa", _sf_dtype(ue8m0), 2), _expect(sfb, "sfb", _sf_dtype(ue8m0), 2)
     k, m = a.shape if a_mn else a.shape[::-1]
     kb_, n = b.shape if b_mn else b.shape[::-1]
     if kb_ != k or tuple(d.shape) != (m, n):
         raise ValueError("shape mismatch between a, b and d")
-    if sfa.shape[0] != k // 128 or tuple(sfb.shape) != _sfb_shape(n, k, False):
-        raise ValueError(f"scale shapes must be sfa [K/128][ld] and sfb {_sfb_shape(n, k, False)}")
+    if sfa.shape[0] != k // 128 or tuple(sfb.shape) != _sfb_shape(n, k, ue8m0):
+        raise ValueError(f"scale shapes must be sfa [K/128][ld] and sfb {_sfb_shape(n, k, ue8m0)}")
     for t, nm in ((a, "a"), (b, "b"), (d, "d"), (sfa, "sfa")):
         _row_major(t, nm)
     _contig(sfb, "sfb")
@@ -241,6 +245,21 @@ def dg_fp8_gemm_tn(a, sfa, b, sfb, d, workspace=None):
 def dg_fp8_gemm_tt(a, sfa, b, sfb, d, workspace=None):
     """d[m][n] = bf16(A^T . B^T) with a stored [K][M] and b [N][K]; NT scale layouts."""
     return _gemm_majors("dg_fp8_gemm_tt", True, False, a, sfa, b, sfb, d, workspace)
+
+
+def dg_fp8_gemm_nn_ue8m0(a, sfa, b, sfb, d, workspace=None):
+    """dg_fp8_gemm_nn with exponent-byte scales (sfb [K/128][ld_sfb] uint8)."""
+    return _gemm_majors("dg_fp8_gemm_nn_ue8m0", False, True, a, sfa, b, sfb, d, workspace, True)
+
+
+def dg_fp8_gemm_tn_ue8m0(a, sfa, b, sfb, d, workspace=None):
+    """dg_fp8_gemm_tn with exponent-byte scales."""
+    return _gemm_majors("dg_fp8_gemm_tn_ue8m0", True, True, a, sfa, b, sfb, d, workspace, True)
+
+
+def dg_fp8_gemm_tt_ue8m0(a, sfa, b, sfb, d, workspace=None):
+    """dg_fp8_gemm_tt with exponent-byte scales."""
+    return _gemm_majors("dg_fp8_gemm_tt_ue8m0", True, False, a, sfa, b, sfb, d, workspace, True)
 
 
 def dg_grouped_contiguous(a, sfa, b, sfb, d, m_indices, workspace=None):
@@ -400,16 +419,25 @@ def dg_quant_1x128(x, q, sf):
     return _quant_1x128("dg_quant_1x128", x, q, sf, False)
 
 
-def dg_quant_1x128_mn(x, q, sf):
-    """x stored [K][M] bf16 -> q [K][M] e4m3, sf [K/128][ld] fp32: 1x128 tiles along K (columns)."""
-    _expect(x, "x", _BF, 2), _expect(q, "q", _U8, 2), _expect(sf, "sf", (torch.float32,), 2)
+def _quant_1x128_mn(fn, x, q, sf, ue8m0):
+    _expect(x, "x", _BF, 2), _expect(q, "q", _U8, 2), _expect(sf, "sf", _sf_dtype(ue8m0), 2)
     rows, cols = x.shape
     if tuple(q.shape) != (rows, cols) or sf.shape[0] != rows // 128:
         raise ValueError("q must match x and sf must be [rows/128][ld]")
     for t, nm in ((x, "x"), (q, "q"), (sf, "sf")):
         _contig(t, nm)
-    _check("dg_quant_1x128_mn", _lib.dg_quant_1x128_mn(_ptr(x), _ptr(q), _ptr(sf), rows, cols, sf.shape[1], _stream(x)))
+    _check(fn, getattr(_lib, fn)(_ptr(x), _ptr(q), _ptr(sf), rows, cols, sf.shape[1], _stream(x)))
     return q, sf
+
+
+def dg_quant_1x128_mn(x, q, sf):
+    """x stored [K][M] bf16 -> q [K][M] e4m3, sf [K/128][ld] fp32: 1x128 tiles along K (columns)."""
+    return _quant_1x128_mn("dg_quant_1x128_mn", x, q, sf, False)
+
+
+def dg_quant_1x128_mn_ue8m0(x, q, sf):
+    """dg_quant_1x128_mn with UE8M0 exponent bytes (sf [K/128][ld] uint8)."""
+    return _quant_1x128_mn("dg_quant_1x128_mn_ue8m0", x, q, sf, True)
 
 
 def dg_quant_1x128_ue8m0(x, q, sf):

@@ -190,9 +190,9 @@ int gemm_nt_impl(const uint8_t* a, const void* sfa, const uint8_t* b, const void
 // Dense GEMM with MN-major operands.  majors bit 0: A is stored M-major as
 // [K][lda] (lda >= m, m % 16 == 0); bit 1: B is stored N-major as [K][ldb]
 // (ldb >= n, n % 16 == 0).  Scales keep the K-major (NT) layouts.
-int gemm_majors_impl(int majors, const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+int gemm_majors_impl(int majors, const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb,
                      uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd, int64_t ld_sfa,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     void* workspace, size_t workspace_bytes, void* stream, bool ue8m0) {
   const bool at = (majors & 1) != 0, bt = (majors & 2) != 0;
   // The common checks see a K-major leading dimension for a transposed
   // operand; its own rules follow.
@@ -214,7 +214,7 @@ int gemm_majors_impl(int majors, const uint8_t* a, const float* sfa, const uint8
   if (m == 0 || n == 0) return ok();
   dg::GemmParams p{};
   p.a = a; p.b = b; p.d = d;
-  set_scales(p, sfa, sfb, n, k, false);
+  set_scales(p, sfa, sfb, n, k, ue8m0);
   p.m = m; p.n = n; p.k = k; p.num_groups = 1;
   p.lda = lda; p.ldb = ldb; p.ldd = ldd; p.ld_sfa = ld_sfa;
   p.majors = majors;
@@ -308,8 +308,8 @@ int quant_1x128_impl(const uint16_t* x, uint8_t* q, void* sf, int rows, int cols
   return ok();
 }
 
-int quant_1x128_mn_impl(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols, int64_t ld_sf,
-                        void* stream) {
+int quant_1x128_mn_impl(const uint16_t* x, uint8_t* q, void* sf, int rows, int cols, int64_t ld_sf,
+                        bool pow2, void* stream) {
   if (rows < 0 || cols < 0) return fail(DG_ERR_INVALID_VALUE, "bad sizes (rows=%d cols=%d)", rows, cols);
   if (rows % 128) return fail(DG_ERR_UNSUPPORTED_SHAPE, "rows=%d (K) is not a multiple of 128", rows);
   if (cols % 8) return fail(DG_ERR_UNSUPPORTED_SHAPE, "cols=%d is not a multiple of 8", cols);
@@ -319,7 +319,7 @@ int quant_1x128_mn_impl(const uint16_t* x, uint8_t* q, float* sf, int rows, int 
   if (!x || !q || !sf) return fail(DG_ERR_INVALID_VALUE, "null pointer argument");
   if (!aligned16(x) || !aligned16(q) || !aligned16(sf)) return fail(DG_ERR_MISALIGNED, "x, q and sf must be 16-byte aligned");
   if (rows == 0 || ld_sf == 0) return ok();
-  const hipError_t e = dg::launch_quant_1x128_mn(x, q, sf, rows, cols, ld_sf, static_cast<hipStream_t>(stream));
+  const hipError_t e = dg::launch_quant_1x128_mn(x, q, sf, rows, cols, ld_sf, pow2, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(DG_ERR_HIP, "quant_1x128_mn launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -352,19 +352,43 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
 int dg_fp8_gemm_nn(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
                    uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
                    int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream) {
-  return gemm_majors_impl(2, a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, workspace, workspace_bytes, stream);
+  return gemm_majors_impl(2, a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, workspace, workspace_bytes, stream,
+                          false);
+}
+
+int dg_fp8_gemm_nn_ue8m0(const uint8_t* a, const uint8_t* sfa, const uint8_t* b, const uint8_t* sfb,
+                         uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
+                         int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_majors_impl(2, a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, workspace, workspace_bytes, stream,
+                          true);
 }
 
 int dg_fp8_gemm_tn(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
                    uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
                    int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream) {
-  return gemm_majors_impl(3, a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, workspace, workspace_bytes, stream);
+  return gemm_majors_impl(3, a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, workspace, workspace_bytes, stream,
+                          false);
+}
+
+int dg_fp8_gemm_tn_ue8m0(const uint8_t* a, const uint8_t* sfa, const uint8_t* b, const uint8_t* sfb,
+                         uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
+                         int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_majors_impl(3, a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, workspace, workspace_bytes, stream,
+                          true);
 }
 
 int dg_fp8_gemm_tt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
                    uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
                    int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream) {
-  return gemm_majors_impl(1, a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, workspace, workspace_bytes, stream);
+  return gemm_majors_impl(1, a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, workspace, workspace_bytes, stream,
+                          false);
+}
+
+int dg_fp8_gemm_tt_ue8m0(const uint8_t* a, const uint8_t* sfa, const uint8_t* b, const uint8_t* sfb,
+                         uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
+                         int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_majors_impl(1, a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, workspace, workspace_bytes, stream,
+                          true);
 }
 
 int dg_fp8_gemm_nt_ue8m0(const uint8_t* a, const uint8_t* sfa, const uint8_t* b,
@@ -450,7 +474,12 @@ int dg_quant_1x128(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
 
 int dg_quant_1x128_mn(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols, int64_t ld_sf,
                       void* stream) {
-  return quant_1x128_mn_impl(x, q, sf, rows, cols, ld_sf, stream);
+  return quant_1x128_mn_impl(x, q, sf, rows, cols, ld_sf, false, stream);
+}
+
+int dg_quant_1x128_mn_ue8m0(const uint16_t* x, uint8_t* q, uint8_t* sf, int rows, int cols, int64_t ld_sf,
+                            void* stream) {
+  return quant_1x128_mn_impl(x, q, sf, rows, cols, ld_sf, true, stream);
 }
 
 int dg_quant_1x128_ue8m0(const uint16_t* x, uint8_t* q, uint8_t* sf, int rows, int cols,

@@ -38,7 +38,7 @@
 // * Layouts: dense, grouped-contiguous (an expert id per row), grouped-masked
 //   (valid rows per expert, read on the device) and K-grouped (an expert's
 //   tokens are a K range; per-row scales on both operands).
-// * Operand majors (dense layout, fp32 scales): A may also be stored M-major
+// * Operand majors (dense layout, fp32 or UE8M0 scales): A may also be stored M-major
 //   ([K][lda]) and B N-major ([K][ldb]), the TN / NN / TT forms of D = A B^T
 //   beside NT.  Such a tile is staged as [128][BM] (K rows of BM bytes) and
 //   its fragments are read with ds_read_b64_tr_b8, gfx950's transposing LDS
@@ -266,11 +266,11 @@ __device__ __forceinline__ const float* scale_ptr(const float* base, int64_t off
 // SF: kScaleF32 (fp32 scales, promoted on the VALU) or kScaleUE8M0 (power-of-
 // two exponents applied inside the block-scaled MFMA, see below).
 // MAJ: operand majors, bit 0 = A stored M-major [K][lda], bit 1 = B stored
-// N-major [K][ldb] (dense layout, fp32 scales).
+// N-major [K][ldb] (dense layout).
 constexpr int kAMajorMN = 1, kBMajorMN = 2;
 template <class T, int LAYOUT, bool SK, int SF, int MAJ = 0>
 __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedule s) {
-  static_assert(MAJ == 0 || (LAYOUT == kDense && SF == kScaleF32), "MN-major operands: dense layout, fp32 scales");
+  static_assert(MAJ == 0 || (LAYOUT == kDense && SF != kScaleRowB), "MN-major operands: dense layout");
   constexpr bool kAT = (MAJ & kAMajorMN) != 0, kBT = (MAJ & kBMajorMN) != 0;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::STAGES * T::kStageBytes];
   __shared__ int last_flag;
@@ -282,6 +282,26 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
   const int fr = lane & 15;  // fragment row (A) / column (B) of this lane
   const int kg = lane >> 4;  // which 32 bytes of the slice
   const int c0 = (2 * kg) ^ (fr & 7), c1 = (2 * kg + 1) ^ (fr & 7);
+  // MFMA operands of a stage at sp: A fragment row i, B fragment column j,
+  // from K-major tiles (two 16-byte reads) or MN-major ones (transposing loads).
+  auto frag_a = [&](const uint8_t* sp, int i) -> v8i {
+    if constexpr (kAT) {
+      return ld_mn_frag<T::BM>(lds_addr(sp), mn_lane_off<T::BM>(fr, kg), wm * T::TM + i * 16);
+    } else {
+      const uint8_t* rowp = sp + (wm * T::TM + i * 16 + fr) * 128;
+      return make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
+                      *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
+    }
+  };
+  auto frag_b = [&](const uint8_t* sp, int j) -> v8i {
+    if constexpr (kBT) {
+      return ld_mn_frag<T::BN>(lds_addr(sp) + T::kBOff, mn_lane_off<T::BN>(fr, kg), wn * T::TN + j * 16);
+    } else {
+      const uint8_t* rowp = sp + T::kBOff + (wn * T::TN + j * 16 + fr) * 128;
+      return make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
+                      *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
+    }
+  };
   const int nkb_total = p.k / kBlockK;
   const int n_blocks = (p.n + kBlockK - 1) / kBlockK;
   const uint32_t smem_base = lds_addr(smem);
@@ -569,16 +589,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
         // scales then load during the last row's MFMAs, and the DMA pieces go
         // out between those MFMAs, so the matrix cores do not drain at the
         // barrier while every wave refetches its operands.
-        auto ld_a = [&](const uint8_t* sp, int i) {
-          const uint8_t* rowp = sp + (wm * T::TM + i * 16 + fr) * 128;
-          return make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
-                          *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
-        };
-        auto ld_b = [&](const uint8_t* sp, int j) {
-          const uint8_t* rowp = sp + T::kBOff + (wn * T::TN + j * 16 + fr) * 128;
-          return make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
-                          *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
-        };
+        auto ld_a = frag_a;
+        auto ld_b = frag_b;
         auto col_block = [&](int j) { return min((n0 + wn * T::TN + j * 16) >> 7, n_blocks - 1); };
         // DMA pieces of the stage issued after the MFMA of column j of the
         // last row: piece q goes out after column q * FN / kIssue.
@@ -700,16 +712,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
               sbe[j] = sbb[min((n0 + wn * T::TN + j * 16) >> 7, n_blocks - 1)];
             v8i bfrag[T::FN];
   #pragma unroll
-            for (int j = 0; j < T::FN; ++j) {
-              const uint8_t* rowp = st + T::kBOff + (wn * T::TN + j * 16 + fr) * 128;
-              bfrag[j] = make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
-                                  *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
-            }
-            auto load_a = [&](int i) {
-              const uint8_t* rowp = st + (wm * T::TM + i * 16 + fr) * 128;
-              return make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
-                              *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
-            };
+            for (int j = 0; j < T::FN; ++j) bfrag[j] = frag_b(st, j);
+            auto load_a = [&](int i) { return frag_a(st, i); };
             auto load_e = [&](int i) { return (int)st[T::kSOff + wm * T::TM + i * 16 + fr]; };
             v8i afrag = load_a(0);
             int ae = load_e(0);
@@ -751,28 +755,12 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
             }
             v8i bfrag[T::FN];
   #pragma unroll
-            for (int j = 0; j < T::FN; ++j) {
-              if constexpr (kBT) {
-                bfrag[j] = ld_mn_frag<T::BN>(lds_addr(st) + T::kBOff, mn_lane_off<T::BN>(fr, kg), wn * T::TN + j * 16);
-              } else {
-                const uint8_t* rowp = st + T::kBOff + (wn * T::TN + j * 16 + fr) * 128;
-                bfrag[j] = make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
-                                    *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
-              }
-            }
+            for (int j = 0; j < T::FN; ++j) bfrag[j] = frag_b(st, j);
             // Software pipeline over the fragment rows: the MFMAs of row i+1 are
             // issued into a second set of result registers before the promotion
             // FMAs of row i, so the matrix core and the VALU overlap instead of
             // each FMA waiting on the MFMA just issued.
-            auto load_a = [&](int i) {
-              if constexpr (kAT) {
-                return ld_mn_frag<T::BM>(lds_addr(st), mn_lane_off<T::BM>(fr, kg), wm * T::TM + i * 16);
-              } else {
-                const uint8_t* rowp = st + (wm * T::TM + i * 16 + fr) * 128;
-                return make_v8i(*reinterpret_cast<const uint4*>(rowp + (c0 << 4)),
-                                *reinterpret_cast<const uint4*>(rowp + (c1 << 4)));
-              }
-            };
+            auto load_a = [&](int i) { return frag_a(st, i); };
             auto load_s = [&](int i) {
               return *reinterpret_cast<const float4*>(st + T::kSOff + (wm * T::TM + i * 16 + 4 * kg) * 4);
             };
@@ -1078,23 +1066,29 @@ hipError_t launch_one(const GemmParams& p, const Schedule& s, int grid, hipStrea
 }
 
 // Dense GEMM with MN-major operands (p.majors: kAMajorMN | kBMajorMN).
-template <class T, int MAJ>
+template <class T, int MAJ, int SF>
 hipError_t launch_majors_one(const GemmParams& p, const Schedule& s, int grid, hipStream_t stream) {
   if (s.stream_k)
-    hipLaunchKernelGGL((gemm_kernel<T, kDense, true, kScaleF32, MAJ>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
+    hipLaunchKernelGGL((gemm_kernel<T, kDense, true, SF, MAJ>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
   else
-    hipLaunchKernelGGL((gemm_kernel<T, kDense, false, kScaleF32, MAJ>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
+    hipLaunchKernelGGL((gemm_kernel<T, kDense, false, SF, MAJ>), dim3(grid), dim3(T::kThreads), 0, stream, p, s);
   return hipGetLastError();
+}
+
+template <class T, int SF>
+hipError_t launch_majors_sf(const GemmParams& p, const Schedule& s, int grid, hipStream_t stream) {
+  switch (p.majors) {
+    case kAMajorMN: return launch_majors_one<T, kAMajorMN, SF>(p, s, grid, stream);
+    case kBMajorMN: return launch_majors_one<T, kBMajorMN, SF>(p, s, grid, stream);
+    case kAMajorMN | kBMajorMN: return launch_majors_one<T, kAMajorMN | kBMajorMN, SF>(p, s, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <class T>
 hipError_t launch_majors(const GemmParams& p, const Schedule& s, int grid, hipStream_t stream) {
-  switch (p.majors) {
-    case kAMajorMN: return launch_majors_one<T, kAMajorMN>(p, s, grid, stream);
-    case kBMajorMN: return launch_majors_one<T, kBMajorMN>(p, s, grid, stream);
-    case kAMajorMN | kBMajorMN: return launch_majors_one<T, kAMajorMN | kBMajorMN>(p, s, grid, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return p.sf_ue8m0 ? launch_majors_sf<T, kScaleUE8M0>(p, s, grid, stream)
+                    : launch_majors_sf<T, kScaleF32>(p, s, grid, stream);
 }
 
 template <class T, int SF>
@@ -1282,8 +1276,8 @@ hipError_t launch_gemm(int layout, const GemmParams& p0, const GemmConfig& cfg,
       default: return hipErrorInvalidValue;
     }
   }
-  if (p.majors) {  // MN-major operands: dense, fp32 scales, the dense heuristic's tiles
-    if (layout != kDense || p.sf_ue8m0) return hipErrorInvalidValue;
+  if (p.majors) {  // MN-major operands: dense layout, the dense heuristic's tiles
+    if (layout != kDense) return hipErrorInvalidValue;
     switch (cfg.variant) {
       case 0: return launch_majors<TileP256>(p, s, cfg.grid, stream);
       case 4: return launch_majors<TileS64>(p, s, cfg.grid, stream);

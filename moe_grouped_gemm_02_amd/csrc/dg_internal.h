@@ -38,7 +38,7 @@ struct GemmParams {
   uint8_t* dq;
   float* dsf;
   int64_t ld_dsf, dq_gstride, dsf_gstride;
-  // Operand majors (dense layout, fp32 scales): bit 0 = A stored M-major as
+  // Operand majors (dense layout): bit 0 = A stored M-major as
   // [K][lda], bit 1 = B stored N-major as [K][ldb]; 0 = both K-major.
   int majors;
 };
@@ -100,9 +100,10 @@ hipError_t launch_gemm(int layout, const GemmParams& p, const GemmConfig& cfg,
 hipError_t launch_quant_1x128(const uint16_t* x, uint8_t* q, void* sf, int rows, int cols,
                               int64_t ld_sf, int groups, bool pow2, hipStream_t stream);
 // x [rows][cols] stored M-major (rows = K, a multiple of 128; cols % 8 == 0):
-// 1x128 tiles along the rows, scales [rows/128][ld_sf].
-hipError_t launch_quant_1x128_mn(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
-                                 int64_t ld_sf, hipStream_t stream);
+// 1x128 tiles along the rows, scales [rows/128][ld_sf] (fp32, or UE8M0
+// exponent bytes with pow2).
+hipError_t launch_quant_1x128_mn(const uint16_t* x, uint8_t* q, void* sf, int rows, int cols,
+                                 int64_t ld_sf, bool pow2, hipStream_t stream);
 hipError_t launch_quant_128x128(const uint16_t* w, uint8_t* q, void* sf, int rows, int cols,
                                 int groups, bool pow2, hipStream_t stream);
 

@@ -109,10 +109,14 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __rest
 // 64 and rows 16 (l / 8) .. + 15, held in registers between the amax and the
 // encode; the 8 lanes of a column group combine their amax with shuffles.
 // Block (x, y): columns [256 x, 256 x + 256), K block y; cols % 8 == 0.
+// POW2: UE8M0 exponent bytes instead of fp32 scales, same [K/128][ld_sf] shape.
+template <bool POW2>
 __global__ __launch_bounds__(256) void quant_1x128_mn_kernel(const uint16_t* __restrict__ x,
                                                              uint8_t* __restrict__ q,
-                                                             float* __restrict__ sf, int rows,
+                                                             void* __restrict__ sf_out, int rows,
                                                              int cols, int64_t ld_sf) {
+  float* sf = static_cast<float*>(sf_out);
+  uint8_t* sf8 = static_cast<uint8_t*>(sf_out);
   const int lane = threadIdx.x & 63;
   const int col = blockIdx.x * 256 + (threadIdx.x >> 6) * 64 + (lane & 7) * 8;
   const int kb = blockIdx.y;
@@ -138,32 +142,55 @@ __global__ __launch_bounds__(256) void quant_1x128_mn_kernel(const uint16_t* __r
     for (int c = 0; c < 8; ++c)
 #pragma unroll
       for (int off = 8; off <= 32; off <<= 1) amax[c] = fmaxf(amax[c], __shfl_xor(amax[c], off, 64));
-    double rcp[8];
-    float s[8];
+    if constexpr (POW2) {
+      uint32_t e[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      s[c] = amax[c] / 448.0f;
-      rcp[c] = tile_reciprocal(s[c]);
-    }
+      for (int c = 0; c < 8; ++c) e[c] = ue8m0_exponent(amax[c]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-      const uint32_t lo = e4m3_x4(quotient(w[0] & 0xFFFFu, rcp[0]), quotient(w[0] >> 16, rcp[1]),
-                                  quotient(w[1] & 0xFFFFu, rcp[2]), quotient(w[1] >> 16, rcp[3]));
-      const uint32_t hi = e4m3_x4(quotient(w[2] & 0xFFFFu, rcp[4]), quotient(w[2] >> 16, rcp[5]),
-                                  quotient(w[3] & 0xFFFFu, rcp[6]), quotient(w[3] >> 16, rcp[7]));
-      *reinterpret_cast<uint2*>(q + (int64_t)(r0 + i) * cols + col) = make_uint2(lo, hi);
-    }
-    if ((lane >> 3) == 0) {
-      float* out = sf + (int64_t)kb * ld_sf + col;
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        const uint32_t lo = e4m3_x4(pow2_quotient(w[0] & 0xFFFFu, e[0]), pow2_quotient(w[0] >> 16, e[1]),
+                                    pow2_quotient(w[1] & 0xFFFFu, e[2]), pow2_quotient(w[1] >> 16, e[3]));
+        const uint32_t hi = e4m3_x4(pow2_quotient(w[2] & 0xFFFFu, e[4]), pow2_quotient(w[2] >> 16, e[5]),
+                                    pow2_quotient(w[3] & 0xFFFFu, e[6]), pow2_quotient(w[3] >> 16, e[7]));
+        *reinterpret_cast<uint2*>(q + (int64_t)(r0 + i) * cols + col) = make_uint2(lo, hi);
+      }
+      if ((lane >> 3) == 0) {
+        uint8_t* out = sf8 + (int64_t)kb * ld_sf + col;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) out[c] = s[c];
+        for (int c = 0; c < 8; ++c) out[c] = (uint8_t)e[c];
+      }
+    } else {
+      double rcp[8];
+      float s[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        s[c] = amax[c] / 448.0f;
+        rcp[c] = tile_reciprocal(s[c]);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        const uint32_t lo = e4m3_x4(quotient(w[0] & 0xFFFFu, rcp[0]), quotient(w[0] >> 16, rcp[1]),
+                                    quotient(w[1] & 0xFFFFu, rcp[2]), quotient(w[1] >> 16, rcp[3]));
+        const uint32_t hi = e4m3_x4(quotient(w[2] & 0xFFFFu, rcp[4]), quotient(w[2] >> 16, rcp[5]),
+                                    quotient(w[3] & 0xFFFFu, rcp[6]), quotient(w[3] >> 16, rcp[7]));
+        *reinterpret_cast<uint2*>(q + (int64_t)(r0 + i) * cols + col) = make_uint2(lo, hi);
+      }
+      if ((lane >> 3) == 0) {
+        float* out = sf + (int64_t)kb * ld_sf + col;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) out[c] = s[c];
+      }
     }
   }
   // Padding entries of the scale matrix (columns in [cols, ld_sf)) are zero.
   const int pad = (int)(ld_sf - cols);
   if (pad > 0 && blockIdx.x == 0 && (int)threadIdx.x < pad) {
-    for (int i = threadIdx.x; i < pad; i += 256) sf[(int64_t)kb * ld_sf + cols + i] = 0.0f;
+    for (int i = threadIdx.x; i < pad; i += 256) {
+      if constexpr (POW2) sf8[(int64_t)kb * ld_sf + cols + i] = 0;
+      else sf[(int64_t)kb * ld_sf + cols + i] = 0.0f;
+    }
   }
 }
 
@@ -248,10 +275,13 @@ hipError_t launch_quant_1x128(const uint16_t* x, uint8_t* q, void* sf, int rows,
   return hipGetLastError();
 }
 
-hipError_t launch_quant_1x128_mn(const uint16_t* x, uint8_t* q, float* sf, int rows, int cols,
-                                 int64_t ld_sf, hipStream_t stream) {
+hipError_t launch_quant_1x128_mn(const uint16_t* x, uint8_t* q, void* sf, int rows, int cols,
+                                 int64_t ld_sf, bool pow2, hipStream_t stream) {
   const dim3 grid((cols + 255) / 256, rows / kBlockK);
-  hipLaunchKernelGGL(quant_1x128_mn_kernel, grid, dim3(256), 0, stream, x, q, sf, rows, cols, ld_sf);
+  if (pow2)
+    hipLaunchKernelGGL(quant_1x128_mn_kernel<true>, grid, dim3(256), 0, stream, x, q, sf, rows, cols, ld_sf);
+  else
+    hipLaunchKernelGGL(quant_1x128_mn_kernel<false>, grid, dim3(256), 0, stream, x, q, sf, rows, cols, ld_sf);
   return hipGetLastError();
 }
 

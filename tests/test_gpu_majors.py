@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import synth
-from oracle import bf16, majors, quant
+from oracle import bf16, majors, quant, ue8m0
 from tests.gpu_util import SENTINEL, bf16_to_f64, dev, host, require_gpu
 from tests.tolerance import check
 
@@ -190,3 +190,64 @@ def test_weight_gradient_shape_sampled():
     ref = np.stack([majors.gemm_layout_ref("nt", a_rows, sa_rows, b_h[[c]], sfb_h[[c // 128]])[:, 0] for c in cols],
                    axis=1)
     check(bf16_to_f64(host(d)[np.ix_(rows, cols)]), ref, "tn 4096x4096x7168 sampled")
+
+
+# --------------------------------------------------------- UE8M0 scales --
+
+UE_VARIANTS = [0, 4, 5, 6]
+
+
+def _ue_operands(m, n, k, seed):
+    a, ea = ue8m0.quant_1x128_ue8m0(synth.bf16_normal((m, k), seed))
+    b, eb = ue8m0.quant_128x128_ue8m0(synth.bf16_normal((n, k), seed + 1))
+    return a, ea, b, eb
+
+
+def _run_ue(dg, layout, a_s, ea, b_s, eb, m, n, k):
+    d = torch.full((m, n), SENTINEL, dtype=torch.int16, device="cuda")
+    getattr(dg, f"dg_fp8_gemm_{layout}_ue8m0")(dev(a_s), dev(ea), dev(b_s), dev(eb), d, workspace=_ws(dg, m, n, k))
+    return host(d)
+
+
+@pytest.mark.parametrize("division", [0, 3])
+@pytest.mark.parametrize("variant", UE_VARIANTS)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_ue8m0_every_variant(layout, variant, division, force):
+    """UE8M0 scales: the same bytes reach the block-scaled MFMA as in NT, so
+    the output equals dg_fp8_gemm_nt_ue8m0's bit for bit; and the oracle,
+    fed the powers of two the exponents stand for, within tolerance."""
+    dg = require_gpu()
+    force(variant, division)
+    m, n, k = 160, 272, 1536
+    a, ea, b, eb = _ue_operands(m, n, k, 1901)
+    a_s, b_s = _stored(layout, a, b)
+    out = _run_ue(dg, layout, a_s, ea, b_s, eb, m, n, k)
+    ref = majors.gemm_layout_ref(layout, a_s, ue8m0.sfa_as_fp32(ea), b_s, ue8m0.sfb_as_fp32(eb, n))
+    check(bf16_to_f64(out), ref, f"{layout} ue8m0 v{variant} d{division}")
+    assert np.array_equal(out, _run_ue(dg, "nt", a, ea, b, eb, m, n, k))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_ue8m0_default_config_decode_and_prefill(layout):
+    dg = require_gpu()
+    for m, n, k in [(64, 2112, 7168), (512, 1024, 2048)]:
+        a, ea, b, eb = _ue_operands(m, n, k, 1911 + m)
+        a_s, b_s = _stored(layout, a, b)
+        out = _run_ue(dg, layout, a_s, ea, b_s, eb, m, n, k)
+        ref = majors.gemm_layout_ref(layout, a_s, ue8m0.sfa_as_fp32(ea), b_s, ue8m0.sfb_as_fp32(eb, n))
+        check(bf16_to_f64(out), ref, f"{layout} ue8m0 {m}x{n}x{k}")
+        assert np.array_equal(out, _run_ue(dg, "nt", a, ea, b, eb, m, n, k))
+
+
+@pytest.mark.parametrize("k,m,ld", [(384, 136, 140), (1024, 4096, 4096)])
+def test_ue8m0_column_quantiser_bitwise(k, m, ld):
+    dg = require_gpu()
+    x = synth.bf16_normal((k, m), 1921 + m)
+    x[0:128, 3] = 0
+    x[128:256, 7] = 0x8000
+    q_ref, sf_ref = majors.quant_1x128_mn_ue8m0(x, ld)
+    q = torch.full((k, m), 0x5A, dtype=torch.uint8, device="cuda")
+    sf = torch.full((k // 128, ld), 0xA5, dtype=torch.uint8, device="cuda")
+    dg.dg_quant_1x128_mn_ue8m0(dev(x), q, sf)
+    assert np.array_equal(host(q), q_ref)
+    assert np.array_equal(host(sf), sf_ref)
