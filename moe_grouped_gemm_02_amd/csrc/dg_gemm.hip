@@ -785,8 +785,22 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
               } else {
                 // MFMAs of row i, then the LDS reads of row i + 1, which complete
                 // while the promotion FMAs of row i run.
+                // 256x256 tiles: the row's MFMAs go out as one block at raised
+                // wave priority, so the SIMD's other wave fills the matrix
+                // core's busy time with its promotion FMAs instead of
+                // competing for issue (prefill 138.3 -> 134.6 us; on the
+                // 128-row tiles the same measured 1-4% slower).
+                constexpr bool kPrio = T::BM * T::BN >= 256 * 256;
+                if constexpr (kPrio) {
+                  __builtin_amdgcn_s_setprio(2);
+                  __builtin_amdgcn_sched_barrier(0);
+                }
   #pragma unroll
                 for (int j = 0; j < T::FN; ++j) part[0][j] = mfma_fp8_slice(afrag, bfrag[j]);
+                if constexpr (kPrio) {
+                  __builtin_amdgcn_sched_barrier(0);
+                  __builtin_amdgcn_s_setprio(0);
+                }
                 if constexpr (i + 1 < T::FM) {
                   afrag = load_a(i + 1);
                   s4 = load_s(i + 1);
