@@ -94,6 +94,10 @@ def parse_args(argv=None):
                    help="only quantise and launch this workload's GEMM --reps times, no timing "
                         "(the program rocprofv3 --pmc runs for the traffic counters)")
     p.add_argument("--reps", type=int, default=5)
+    p.add_argument("--write-mfma", metavar="PMC_CSV",
+                   help="with --launches-only W: write profiles/gemm_kernel_W_mfma.txt from a counter pass "
+                        "over the MFMA counters (see write_mfma)")
+    p.add_argument("--num-cus", type=int, default=256, help="CUs of the measured GPU, for --write-mfma")
     p.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                    help="write the traffic summary for --launches-only's workload from four rocprofv3 "
                         "counter_collection.csv files (no GPU needed)")
@@ -497,10 +501,50 @@ def write_traffic(workload, scales, fetch_csv, write_csv, copy_fetch_csv, copy_w
     print(path)
 
 
-def read_traffic(workload, scales="fp32"):
-    """Bytes per launch from the committed summary, or None if there is none
-    for this workload or the kernel sources changed since it was taken."""
-    path = traffic_path(workload, scales)
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_INSTS_VALU_MFMA_MOPS_F6F4 SQ_INSTS_MFMA "
+                 "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_BUSY_CYCLES GRBM_GUI_ACTIVE")
+MI355X_XCDS = 8
+
+
+def mfma_path(workload, scales="fp32"):
+    return os.path.join(PROFILES, f"gemm_kernel_{workload}{'_ue8m0' if scales == 'ue8m0' else ''}_mfma.txt")
+
+
+def write_mfma(workload, scales, pmc_csv, num_cus):
+    """MFMA-busy fraction of one workload's GEMM launches from a counter pass:
+    SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) / (GRBM_GUI_ACTIVE per XCD x
+    SIMDs), medians over the dispatches; plus the MFMA op count against the
+    algorithmic flops."""
+    busy, nd = _counter_per_dispatch(pmc_csv, "SQ_VALU_MFMA_BUSY_CYCLES", "gemm_kernel")
+    gui, _ = _counter_per_dispatch(pmc_csv, "GRBM_GUI_ACTIVE", "gemm_kernel")
+    mops, _ = _counter_per_dispatch(pmc_csv, "SQ_INSTS_VALU_MFMA_MOPS_F8", "gemm_kernel")
+    simds = 4 * num_cus
+    frac = busy / (gui / MI355X_XCDS * simds)
+    sflag = " --scales ue8m0" if scales == "ue8m0" else ""
+    lines = [
+        f"workload={workload}",
+        f"scales={scales}",
+        f"kernel_source_sha256_16={kernel_source_hash()}",
+        f"mfma_busy_cycles={busy:.6g}  (SQ_VALU_MFMA_BUSY_CYCLES, median of {nd} dispatches, all SIMDs)",
+        f"grbm_gui_active={gui:.6g}  (summed over {MI355X_XCDS} XCDs)",
+        f"simds={simds}",
+        f"mfma_busy_frac={frac:.4f}",
+        f"mfma_flops={mops * 512:.6g}  (SQ_INSTS_VALU_MFMA_MOPS_F8 x 512)",
+        "",
+        "commands (from the repository root, REPO = its absolute path):",
+        "  cd /tmp && export TMPDIR=/tmp",
+        f"  rocprofv3 --pmc {MFMA_COUNTERS} -f csv -d $REPO/gpurun_out/pmcm -o p -- python3 $REPO/bench.py --launches-only {workload}{sflag}",
+        f"  python3 bench.py --launches-only {workload}{sflag} --write-mfma gpurun_out/pmcm/p_counter_collection.csv",
+    ]
+    path = mfma_path(workload, scales)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+
+
+def _read_summary(path, key):
+    """A value from a committed counter summary, or None if there is none or
+    the kernel sources changed since it was taken."""
     if not os.path.exists(path):
         return None
     fields = {}
@@ -511,7 +555,17 @@ def read_traffic(workload, scales="fp32"):
                 fields[k.strip()] = v.split()[0]
     if fields.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return float(fields["traffic_bytes_per_launch"])
+    return float(fields[key])
+
+
+def read_mfma_busy(workload, scales="fp32"):
+    return _read_summary(mfma_path(workload, scales), "mfma_busy_frac")
+
+
+def read_traffic(workload, scales="fp32"):
+    """Bytes per launch from the committed summary, or None if there is none
+    for this workload or the kernel sources changed since it was taken."""
+    return _read_summary(traffic_path(workload, scales), "traffic_bytes_per_launch")
 
 
 def main(argv=None):
@@ -520,6 +574,11 @@ def main(argv=None):
         if not args.launches_only:
             raise SystemExit("--write-traffic needs --launches-only WORKLOAD")
         write_traffic(args.launches_only, args.scales, *args.write_traffic)
+        return 0
+    if args.write_mfma:
+        if not args.launches_only:
+            raise SystemExit("--write-mfma needs --launches-only WORKLOAD")
+        write_mfma(args.launches_only, args.scales, args.write_mfma, args.num_cus)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -605,6 +664,10 @@ def main(argv=None):
     # has a summary taken with the current kernel sources.
     measured = [read_traffic(preps[i].wl.name, args.scales) for i in idx]
     traffic = float(np.mean(measured)) if measured and all(x is not None for x in measured) else None
+    # Counter-measured MFMA-busy fraction (matrix-core busy cycles over elapsed
+    # cycles x SIMDs, at the clock the GPU actually ran), same condition.
+    busy = [read_mfma_busy(preps[i].wl.name, args.scales) for i in idx]
+    mfma_busy = float(np.mean(busy)) if busy and all(x is not None for x in busy) else None
     roofline = {
         "bound": "mfma" if mfma_bound else "hbm",
         "achieved": round(achieved, 1),
@@ -612,6 +675,7 @@ def main(argv=None):
         "unit": "TFLOP/s" if mfma_bound else "GB/s",
         "frac": round(achieved / peak, 4),
         "traffic": round(traffic) if traffic is not None else None,
+        "mfma_busy_frac": round(mfma_busy, 4) if mfma_busy is not None else None,
         "traffic_source": ([os.path.relpath(traffic_path(preps[i].wl.name, args.scales), os.path.dirname(PROFILES))
                             for i in idx]
                            if traffic is not None else None),
