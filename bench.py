@@ -393,7 +393,7 @@ def cpu_baseline(wls, target_s, scales="fp32"):
     secs = 0.0
     runs = 0
     with threadpool_limits(limits=1):
-        while secs < target_s and runs < 20 * len(samples):
+        while secs < target_s and runs < 50 * len(samples):
             wl, m, ncols, xa, qb, sfb = samples[runs % len(samples)]
             t0 = time.perf_counter()
             qa, sfa = quant_a(xa)
