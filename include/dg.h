@@ -182,6 +182,29 @@ int dg_grouped_masked_qout(const uint8_t* a, const float* sfa, const uint8_t* b,
                            int64_t ld_dsf, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The UE8M0 GEMMs with a quantised copy of their output in the same format:
+ * input scales as for the *_ue8m0 entry points, and every 1x128 tile of the
+ * bf16 output quantised exactly as dg_quant_1x128_ue8m0 would quantise d
+ * (E = ceil(log2(amax / 448)) + 127 clamped to [0, 254], q = e4m3(x / 2^(E-127))).
+ *   dq  as for the *_qout entry points
+ *   dsf uint8 exponents [n/128][ld_dsf] (masked: [num_groups][n/128][ld_dsf])
+ * Rules, written rows and scale padding as for the *_qout entry points.
+ */
+int dg_fp8_gemm_nt_ue8m0_qout(const uint8_t* a, const uint8_t* sfa, const uint8_t* b, const uint8_t* sfb,
+                              uint16_t* d, uint8_t* dq, uint8_t* dsf, int m, int n, int k, int64_t lda,
+                              int64_t ldb, int64_t ldd, int64_t ld_sfa, int64_t ld_dsf, void* workspace,
+                              size_t workspace_bytes, void* stream);
+int dg_grouped_contiguous_ue8m0_qout(const uint8_t* a, const uint8_t* sfa, const uint8_t* b,
+                                     const uint8_t* sfb, uint16_t* d, uint8_t* dq, uint8_t* dsf,
+                                     const int32_t* m_indices, int m_total, int n, int k, int num_groups,
+                                     int64_t ld_sfa, int64_t ld_dsf, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+int dg_grouped_masked_ue8m0_qout(const uint8_t* a, const uint8_t* sfa, const uint8_t* b, const uint8_t* sfb,
+                                 uint16_t* d, uint8_t* dq, uint8_t* dsf, const int32_t* masked_m,
+                                 int num_groups, int m_max, int n, int k, int expected_m, int64_t ld_sfa,
+                                 int64_t ld_dsf, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * K-axis grouped GEMM (the weight-gradient GEMM of MoE training): the tokens
  * of all experts are concatenated along K, and group g owns the K range
  * [k_offsets[g], k_offsets[g+1]).  The pages name grouping along K next to

@@ -40,6 +40,9 @@ _SIGNATURES = {
     "dg_fp8_gemm_nt_qout": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _L, _L, _L, _P, _S, _P]),
     "dg_grouped_contiguous_qout": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _L, _P, _S, _P]),
     "dg_grouped_masked_qout": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _P, _S, _P]),
+    "dg_fp8_gemm_nt_ue8m0_qout": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _L, _L, _L, _P, _S, _P]),
+    "dg_grouped_contiguous_ue8m0_qout": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _L, _P, _S, _P]),
+    "dg_grouped_masked_ue8m0_qout": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _L, _P, _S, _P]),
     "dg_k_grouped_nt": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _L, _P, _S, _P]),
     "dg_fp8_gemm_nn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _L, _L, _P, _S, _P]),
     "dg_fp8_gemm_tn": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _L, _L, _P, _S, _P]),
@@ -282,9 +285,10 @@ def dg_grouped_masked_ue8m0(a, sfa, b, sfb, d, masked_m, expected_m=0, workspace
     return _masked("dg_grouped_masked_ue8m0", a, sfa, b, sfb, d, masked_m, expected_m, workspace, True)
 
 
-def _check_qout(dq, dsf, rows_shape, n, grouped):
-    """dq e4m3 [(G)][rows][n] contiguous, dsf fp32 [(G)][n/128][ld]; returns ld."""
-    _expect(dq, "dq", _U8, len(rows_shape) + 1), _expect(dsf, "dsf", (torch.float32,), len(rows_shape) + 1)
+def _check_qout(dq, dsf, rows_shape, n, grouped, ue8m0=False):
+    """dq e4m3 [(G)][rows][n] contiguous, dsf [(G)][n/128][ld] (fp32, or uint8
+    exponents with ue8m0); returns ld."""
+    _expect(dq, "dq", _U8, len(rows_shape) + 1), _expect(dsf, "dsf", _sf_dtype(ue8m0), len(rows_shape) + 1)
     if tuple(dq.shape) != tuple(rows_shape) + (n,):
         raise ValueError(f"dq must have shape {tuple(rows_shape) + (n,)}")
     want = ((rows_shape[0],) if grouped else ()) + (n // 128,)
@@ -294,51 +298,49 @@ def _check_qout(dq, dsf, rows_shape, n, grouped):
     return dsf.shape[-1]
 
 
-def dg_fp8_gemm_nt_qout(a, sfa, b, sfb, d, dq, dsf, workspace=None):
-    """dg_fp8_gemm_nt that also writes the 1x128 quantisation of d: dq [M][N], dsf [N/128][ld]."""
+def _gemm_nt_qout(fn, a, sfa, b, sfb, d, dq, dsf, workspace, ue8m0):
     _expect(a, "a", _U8, 2), _expect(b, "b", _U8, 2), _expect(d, "d", _BF, 2)
-    _expect(sfa, "sfa", (torch.float32,), 2), _expect(sfb, "sfb", (torch.float32,), 2)
+    _expect(sfa, "sfa", _sf_dtype(ue8m0), 2), _expect(sfb, "sfb", _sf_dtype(ue8m0), 2)
     m, k = a.shape
     n = b.shape[0]
     if b.shape[1] != k or tuple(d.shape) != (m, n):
         raise ValueError("shape mismatch between a, b and d")
-    if sfa.shape[0] != k // 128 or tuple(sfb.shape) != _sfb_shape(n, k, False):
-        raise ValueError("scale shapes must be sfa [K/128][ld] and sfb [ceil(N/128)][K/128]")
+    if sfa.shape[0] != k // 128 or tuple(sfb.shape) != _sfb_shape(n, k, ue8m0):
+        raise ValueError(f"scale shapes must be sfa [K/128][ld] and sfb {_sfb_shape(n, k, ue8m0)}")
     for t, nm in ((a, "a"), (b, "b"), (d, "d"), (sfa, "sfa")):
         _row_major(t, nm)
     _contig(sfb, "sfb")
-    ld_dsf = _check_qout(dq, dsf, (m,), n, False)
-    _check("dg_fp8_gemm_nt_qout", _lib.dg_fp8_gemm_nt_qout(
+    ld_dsf = _check_qout(dq, dsf, (m,), n, False, ue8m0)
+    _check(fn, getattr(_lib, fn)(
         _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), _ptr(dq), _ptr(dsf), m, n, k, a.stride(0),
         b.stride(0), d.stride(0), sfa.stride(0), ld_dsf, _ptr(workspace), _ws(workspace), _stream(d)))
     return d, dq, dsf
 
 
-def dg_grouped_contiguous_qout(a, sfa, b, sfb, d, dq, dsf, m_indices, workspace=None):
-    """dg_grouped_contiguous that also writes the 1x128 quantisation of d."""
+def _contiguous_qout(fn, a, sfa, b, sfb, d, dq, dsf, m_indices, workspace, ue8m0):
     _expect(a, "a", _U8, 2), _expect(b, "b", _U8, 3), _expect(d, "d", _BF, 2)
-    _expect(sfa, "sfa", (torch.float32,), 2), _expect(sfb, "sfb", (torch.float32,), 3)
+    _expect(sfa, "sfa", _sf_dtype(ue8m0), 2), _expect(sfb, "sfb", _sf_dtype(ue8m0), 3)
     _expect(m_indices, "m_indices", (torch.int32,), 1)
     m_total, k = a.shape
     groups, n = b.shape[0], b.shape[1]
     if b.shape[2] != k or tuple(d.shape) != (m_total, n) or m_indices.shape[0] != m_total:
         raise ValueError("shape mismatch between a, b, d and m_indices")
-    if sfa.shape[0] != k // 128 or tuple(sfb.shape) != (groups,) + _sfb_shape(n, k, False):
-        raise ValueError("scale shapes must be sfa [K/128][ld] and sfb [G][ceil(N/128)][K/128]")
+    want_b = (groups,) + _sfb_shape(n, k, ue8m0)
+    if sfa.shape[0] != k // 128 or tuple(sfb.shape) != want_b:
+        raise ValueError(f"scale shapes must be sfa [K/128][ld] and sfb {want_b}")
     for t, nm in ((a, "a"), (b, "b"), (d, "d"), (sfb, "sfb"), (m_indices, "m_indices")):
         _contig(t, nm)
     _row_major(sfa, "sfa")
-    ld_dsf = _check_qout(dq, dsf, (m_total,), n, False)
-    _check("dg_grouped_contiguous_qout", _lib.dg_grouped_contiguous_qout(
+    ld_dsf = _check_qout(dq, dsf, (m_total,), n, False, ue8m0)
+    _check(fn, getattr(_lib, fn)(
         _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), _ptr(dq), _ptr(dsf), _ptr(m_indices), m_total, n, k,
         groups, sfa.stride(0), ld_dsf, _ptr(workspace), _ws(workspace), _stream(d)))
     return d, dq, dsf
 
 
-def dg_grouped_masked_qout(a, sfa, b, sfb, d, dq, dsf, masked_m, expected_m=0, workspace=None):
-    """dg_grouped_masked that also writes the 1x128 quantisation of d: dq [G][M_max][N], dsf [G][N/128][ld]."""
+def _masked_qout(fn, a, sfa, b, sfb, d, dq, dsf, masked_m, expected_m, workspace, ue8m0):
     _expect(a, "a", _U8, 3), _expect(b, "b", _U8, 3), _expect(d, "d", _BF, 3)
-    _expect(sfa, "sfa", (torch.float32,), 3), _expect(sfb, "sfb", (torch.float32,), 3)
+    _expect(sfa, "sfa", _sf_dtype(ue8m0), 3), _expect(sfb, "sfb", _sf_dtype(ue8m0), 3)
     _expect(masked_m, "masked_m", (torch.int32,), 1)
     groups, m_max, k = a.shape
     n = b.shape[1]
@@ -346,15 +348,48 @@ def dg_grouped_masked_qout(a, sfa, b, sfb, d, dq, dsf, masked_m, expected_m=0, w
         raise ValueError("shape mismatch between a, b and d")
     if masked_m.shape[0] != groups:
         raise ValueError("masked_m must have one entry per group")
-    if sfa.shape[:2] != (groups, k // 128) or tuple(sfb.shape) != (groups,) + _sfb_shape(n, k, False):
-        raise ValueError("scale shapes must be sfa [G][K/128][ld] and sfb [G][ceil(N/128)][K/128]")
+    want_b = (groups,) + _sfb_shape(n, k, ue8m0)
+    if sfa.shape[:2] != (groups, k // 128) or tuple(sfb.shape) != want_b:
+        raise ValueError(f"scale shapes must be sfa [G][K/128][ld] and sfb {want_b}")
     for t, nm in ((a, "a"), (b, "b"), (d, "d"), (sfa, "sfa"), (sfb, "sfb"), (masked_m, "masked_m")):
         _contig(t, nm)
-    ld_dsf = _check_qout(dq, dsf, (groups, m_max), n, True)
-    _check("dg_grouped_masked_qout", _lib.dg_grouped_masked_qout(
+    ld_dsf = _check_qout(dq, dsf, (groups, m_max), n, True, ue8m0)
+    _check(fn, getattr(_lib, fn)(
         _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), _ptr(dq), _ptr(dsf), _ptr(masked_m), groups, m_max, n, k,
         int(expected_m), sfa.shape[2], ld_dsf, _ptr(workspace), _ws(workspace), _stream(d)))
     return d, dq, dsf
+
+
+def dg_fp8_gemm_nt_qout(a, sfa, b, sfb, d, dq, dsf, workspace=None):
+    """dg_fp8_gemm_nt that also writes the 1x128 quantisation of d: dq [M][N], dsf [N/128][ld]."""
+    return _gemm_nt_qout("dg_fp8_gemm_nt_qout", a, sfa, b, sfb, d, dq, dsf, workspace, False)
+
+
+def dg_grouped_contiguous_qout(a, sfa, b, sfb, d, dq, dsf, m_indices, workspace=None):
+    """dg_grouped_contiguous that also writes the 1x128 quantisation of d."""
+    return _contiguous_qout("dg_grouped_contiguous_qout", a, sfa, b, sfb, d, dq, dsf, m_indices, workspace, False)
+
+
+def dg_grouped_masked_qout(a, sfa, b, sfb, d, dq, dsf, masked_m, expected_m=0, workspace=None):
+    """dg_grouped_masked that also writes the 1x128 quantisation of d: dq [G][M_max][N], dsf [G][N/128][ld]."""
+    return _masked_qout("dg_grouped_masked_qout", a, sfa, b, sfb, d, dq, dsf, masked_m, expected_m, workspace, False)
+
+
+def dg_fp8_gemm_nt_ue8m0_qout(a, sfa, b, sfb, d, dq, dsf, workspace=None):
+    """dg_fp8_gemm_nt_ue8m0 that also writes d's 1x128 UE8M0 quantisation (dsf uint8 exponents)."""
+    return _gemm_nt_qout("dg_fp8_gemm_nt_ue8m0_qout", a, sfa, b, sfb, d, dq, dsf, workspace, True)
+
+
+def dg_grouped_contiguous_ue8m0_qout(a, sfa, b, sfb, d, dq, dsf, m_indices, workspace=None):
+    """dg_grouped_contiguous_ue8m0 that also writes d's 1x128 UE8M0 quantisation."""
+    return _contiguous_qout("dg_grouped_contiguous_ue8m0_qout", a, sfa, b, sfb, d, dq, dsf, m_indices, workspace,
+                            True)
+
+
+def dg_grouped_masked_ue8m0_qout(a, sfa, b, sfb, d, dq, dsf, masked_m, expected_m=0, workspace=None):
+    """dg_grouped_masked_ue8m0 that also writes d's 1x128 UE8M0 quantisation."""
+    return _masked_qout("dg_grouped_masked_ue8m0_qout", a, sfa, b, sfb, d, dq, dsf, masked_m, expected_m,
+                        workspace, True)
 
 
 def dg_k_grouped_nt(a, sfa, b, sfb, d, k_offsets, workspace=None):

@@ -135,8 +135,9 @@ int run_gemm(int layout, dg::GemmParams& p, int rows, int groups, void* ws, size
 // Optional quantised copy of the output (the *_qout entry points).
 struct QOut {
   uint8_t* dq;
-  float* dsf;
+  void* dsf;
   int64_t ld_dsf;
+  bool ue8m0;  // exponent-byte output scales
 };
 
 // Checks of the quantised-output arguments; rows = the rows of one group.
@@ -154,7 +155,8 @@ int check_qout(const QOut* q, int rows, int n, int groups) {
 void set_qout(dg::GemmParams& p, const QOut* q, int rows, int n) {
   if (!q) return;
   p.dq = q->dq;
-  p.dsf = q->dsf;
+  p.dsf = static_cast<float*>(q->dsf);
+  p.dq_ue8m0 = q->ue8m0 ? 1 : 0;
   p.ld_dsf = q->ld_dsf;
   p.dq_gstride = (int64_t)rows * n;
   p.dsf_gstride = (int64_t)(n / 128) * q->ld_dsf;
@@ -436,9 +438,18 @@ int dg_fp8_gemm_nt_qout(const uint8_t* a, const float* sfa, const uint8_t* b, co
                         uint16_t* d, uint8_t* dq, float* dsf, int m, int n, int k, int64_t lda,
                         int64_t ldb, int64_t ldd, int64_t ld_sfa, int64_t ld_dsf, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  const QOut q{dq, dsf, ld_dsf};
+  const QOut q{dq, dsf, ld_dsf, false};
   return gemm_nt_impl(a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, workspace, workspace_bytes,
                       stream, false, &q);
+}
+
+int dg_fp8_gemm_nt_ue8m0_qout(const uint8_t* a, const uint8_t* sfa, const uint8_t* b, const uint8_t* sfb,
+                              uint16_t* d, uint8_t* dq, uint8_t* dsf, int m, int n, int k, int64_t lda,
+                              int64_t ldb, int64_t ldd, int64_t ld_sfa, int64_t ld_dsf, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  const QOut q{dq, dsf, ld_dsf, true};
+  return gemm_nt_impl(a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, workspace, workspace_bytes,
+                      stream, true, &q);
 }
 
 int dg_grouped_contiguous_qout(const uint8_t* a, const float* sfa, const uint8_t* b,
@@ -446,18 +457,37 @@ int dg_grouped_contiguous_qout(const uint8_t* a, const float* sfa, const uint8_t
                                const int32_t* m_indices, int m_total, int n, int k, int num_groups,
                                int64_t ld_sfa, int64_t ld_dsf, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  const QOut q{dq, dsf, ld_dsf};
+  const QOut q{dq, dsf, ld_dsf, false};
   return contiguous_impl(a, sfa, b, sfb, d, m_indices, m_total, n, k, num_groups, ld_sfa, workspace,
                          workspace_bytes, stream, false, &q);
+}
+
+int dg_grouped_contiguous_ue8m0_qout(const uint8_t* a, const uint8_t* sfa, const uint8_t* b,
+                                     const uint8_t* sfb, uint16_t* d, uint8_t* dq, uint8_t* dsf,
+                                     const int32_t* m_indices, int m_total, int n, int k, int num_groups,
+                                     int64_t ld_sfa, int64_t ld_dsf, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  const QOut q{dq, dsf, ld_dsf, true};
+  return contiguous_impl(a, sfa, b, sfb, d, m_indices, m_total, n, k, num_groups, ld_sfa, workspace,
+                         workspace_bytes, stream, true, &q);
 }
 
 int dg_grouped_masked_qout(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
                            uint16_t* d, uint8_t* dq, float* dsf, const int32_t* masked_m,
                            int num_groups, int m_max, int n, int k, int expected_m, int64_t ld_sfa,
                            int64_t ld_dsf, void* workspace, size_t workspace_bytes, void* stream) {
-  const QOut q{dq, dsf, ld_dsf};
+  const QOut q{dq, dsf, ld_dsf, false};
   return masked_impl(a, sfa, b, sfb, d, masked_m, num_groups, m_max, n, k, expected_m, ld_sfa,
                      workspace, workspace_bytes, stream, false, &q);
+}
+
+int dg_grouped_masked_ue8m0_qout(const uint8_t* a, const uint8_t* sfa, const uint8_t* b, const uint8_t* sfb,
+                                 uint16_t* d, uint8_t* dq, uint8_t* dsf, const int32_t* masked_m,
+                                 int num_groups, int m_max, int n, int k, int expected_m, int64_t ld_sfa,
+                                 int64_t ld_dsf, void* workspace, size_t workspace_bytes, void* stream) {
+  const QOut q{dq, dsf, ld_dsf, true};
+  return masked_impl(a, sfa, b, sfb, d, masked_m, num_groups, m_max, n, k, expected_m, ld_sfa,
+                     workspace, workspace_bytes, stream, true, &q);
 }
 
 int dg_k_grouped_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb, uint16_t* d,

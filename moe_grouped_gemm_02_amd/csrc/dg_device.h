@@ -53,4 +53,25 @@ __device__ __forceinline__ uint32_t e4m3_x4(float a, float b, float c, float d) 
   return (uint32_t)w;
 }
 
+// Power-of-two (UE8M0) scales: E = ceil(log2(amax / 448)) + 127, clamped to
+// [0, 254], 0 for an all-zero tile; the scale is 2^(E - 127).  The quotient
+// amax/448 is formed in fp64: for a bf16 amax it is either exactly a power of
+// two (amax = 7 * 2^j) or at least 2^-11 (relative) away from one, so the
+// fp64 rounding cannot move it across a power of two.
+__device__ __forceinline__ uint32_t ue8m0_exponent(float amax) {
+  if (amax == 0.0f) return 0u;
+  const double v = (double)amax / 448.0;
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  int e = (int)((u >> 52) & 0x7FF) - 1023;  // v is a normal fp64 number
+  if (u & 0xFFFFFFFFFFFFFull) e += 1;       // not a power of two: round up
+  e += 127;
+  return (uint32_t)(e < 0 ? 0 : (e > 254 ? 254 : e));
+}
+
+// x / 2^(E - 127): exact in fp32 except below the normal range, where
+// v_ldexp_f32 rounds to nearest even.
+__device__ __forceinline__ float pow2_quotient(uint32_t bf16_bits, uint32_t e) {
+  return __builtin_ldexpf(bf16_bits_to_f32(bf16_bits), 127 - (int)e);
+}
+
 }  // namespace dg

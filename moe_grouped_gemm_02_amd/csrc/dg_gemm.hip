@@ -412,7 +412,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
     const float* SA = p.sfa;
     uint16_t* D = p.d;
     uint8_t* DQ = p.dq;
-    float* DSF = p.dsf;
+    // Output scales: fp32, or UE8M0 exponent bytes (p.dq_ue8m0); addressed
+    // in bytes so both formats share the strides counted in elements.
+    const int dsf_esize = p.dq_ue8m0 ? 1 : 4;
+    uint8_t* DSF = reinterpret_cast<uint8_t*>(p.dsf);
     if (LAYOUT == kKGrouped) D += (int64_t)g * p.d_gstride;
     if (LAYOUT == kMasked) {
       rows_valid = clamp_rows(p.masked_m[g], p.m);
@@ -421,7 +424,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
       D += (int64_t)g * p.d_gstride;
       if (DQ) {
         DQ += (int64_t)g * p.dq_gstride;
-        DSF += (int64_t)g * p.dsf_gstride;
+        DSF += (int64_t)g * p.dsf_gstride * dsf_esize;
       }
     }
     // Contiguous layout: the experts of the tile's 128-row halves.  A tile
@@ -1004,16 +1007,32 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
                 amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w[e] & 0xFFFFu)), fabsf(bf16_bits_to_f32(w[e] >> 16))));
 #pragma unroll
               for (int off = 4; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 8));
-              const float s_out = amax / 448.0f;
-              const double rcp = tile_reciprocal(s_out);
               uint32_t out[4];
+              float s_out = 0.0f;
+              uint32_t e_out = 0u;
+              if (p.dq_ue8m0) {
+                // Power-of-two scale 2^(E - 127), E as the UE8M0 quantiser picks it.
+                e_out = ue8m0_exponent(amax);
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                out[e] = e4m3_x4(quotient(w[2 * e] & 0xFFFFu, rcp), quotient(w[2 * e] >> 16, rcp),
-                                 quotient(w[2 * e + 1] & 0xFFFFu, rcp), quotient(w[2 * e + 1] >> 16, rcp));
+                for (int e = 0; e < 4; ++e)
+                  out[e] = e4m3_x4(pow2_quotient(w[2 * e] & 0xFFFFu, e_out), pow2_quotient(w[2 * e] >> 16, e_out),
+                                   pow2_quotient(w[2 * e + 1] & 0xFFFFu, e_out),
+                                   pow2_quotient(w[2 * e + 1] >> 16, e_out));
+              } else {
+                s_out = amax / 448.0f;
+                const double rcp = tile_reciprocal(s_out);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  out[e] = e4m3_x4(quotient(w[2 * e] & 0xFFFFu, rcp), quotient(w[2 * e] >> 16, rcp),
+                                   quotient(w[2 * e + 1] & 0xFFFFu, rcp), quotient(w[2 * e + 1] >> 16, rcp));
+              }
               if (ok) {
                 *reinterpret_cast<uint4*>(DQ + (int64_t)row * p.n + col) = make_uint4(out[0], out[1], out[2], out[3]);
-                if ((qc & 7) == 0) DSF[(int64_t)(col >> 7) * p.ld_dsf + row] = s_out;
+                if ((qc & 7) == 0) {
+                  const int64_t at = (int64_t)(col >> 7) * p.ld_dsf + row;
+                  if (p.dq_ue8m0) DSF[at] = (uint8_t)e_out;
+                  else reinterpret_cast<float*>(DSF)[at] = s_out;
+                }
               }
             }
           }
@@ -1026,7 +1045,11 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
           const int pad = (int)(p.ld_dsf - p.m);
           for (int idx = tid; idx < pad * (T::BN / 128); idx += T::kThreads) {
             const int cb = (n0 >> 7) + idx / pad;
-            if (cb * 128 < p.n) DSF[(int64_t)cb * p.ld_dsf + p.m + idx % pad] = 0.0f;
+            if (cb * 128 < p.n) {
+              const int64_t at = (int64_t)cb * p.ld_dsf + p.m + idx % pad;
+              if (p.dq_ue8m0) DSF[at] = 0;
+              else reinterpret_cast<float*>(DSF)[at] = 0.0f;
+            }
           }
         }
       }

@@ -38,6 +38,7 @@ struct GemmParams {
   uint8_t* dq;
   float* dsf;
   int64_t ld_dsf, dq_gstride, dsf_gstride;
+  int dq_ue8m0;  // 1: dsf holds UE8M0 exponent bytes (same shape and strides in elements)
   // Operand majors (dense layout): bit 0 = A stored M-major as
   // [K][lda], bit 1 = B stored N-major as [K][ldb]; 0 = both K-major.
   int majors;

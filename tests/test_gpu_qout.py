@@ -26,7 +26,7 @@ import pytest
 import torch
 
 import synth
-from oracle import bf16, e4m3, gemm, quant
+from oracle import bf16, e4m3, gemm, quant, ue8m0
 from tests.gpu_util import SENTINEL, bf16_to_f64, dev, host, require_gpu
 from tests.tolerance import check
 
@@ -202,3 +202,105 @@ def test_random_inputs(m, n, k):
     rms = np.sqrt(np.mean(d64 ** 2))
     bound = 1e-2 * rms + (2.0 ** -8 + 2.0 ** -4) * np.abs(ref) + 2.0 ** -9 * sf_h[:, :m].T[:, :, None]
     assert np.all(np.abs(deq - ref) <= bound)
+
+
+# ------------------------------------------------- UE8M0 output scales --
+
+UE_QOUT_VARIANTS = [0, 1, 5, 6]  # built with UE8M0 scales and whole 128-column blocks
+
+
+@pytest.fixture(scope="module")
+def exact_dense_ue8m0():
+    a, ea = ue8m0.quant_1x128_ue8m0(synth.bf16_grid((M, K), 851))
+    b, eb = ue8m0.quant_128x128_ue8m0(synth.bf16_grid((N, K), 852))
+    assert np.all(ea[:, :M] == 119) and np.all(eb[:, :(N + 127) // 128] == 119)  # 2^-8 everywhere
+    d64 = gemm.gemm_nt_ref(a, ue8m0.sfa_as_fp32(ea), b, ue8m0.sfb_as_fp32(eb, N))
+    assert np.all(d64 * 16 == np.round(d64 * 16)) and np.abs(d64).max() < 2.0 ** 19
+    d_bits = bf16.bits_from_f64(d64)
+    ld = quant.sf_leading_dim(M) + 4
+    q_ref, e_ref = ue8m0.quant_1x128_ue8m0(d_bits, ld_sf=ld)
+    return a, ea, b, eb, d_bits, q_ref, e_ref, ld
+
+
+def _ue_outputs(shape, n, ld):
+    d = torch.full(shape + (n,), SENTINEL, dtype=torch.int16, device="cuda")
+    dq = torch.full(shape + (n,), Q_SENT, dtype=torch.uint8, device="cuda")
+    dsf_shape = ((shape[0],) if len(shape) == 2 else ()) + (n // 128, ld)
+    dsf = torch.full(dsf_shape, 0xA5, dtype=torch.uint8, device="cuda")
+    return d, dq, dsf
+
+
+@pytest.mark.parametrize("division", [0, 1, 3])
+@pytest.mark.parametrize("variant", UE_QOUT_VARIANTS)
+def test_ue8m0_exact_dense_every_variant(variant, division, force, exact_dense_ue8m0):
+    dg = require_gpu()
+    force(variant, division)
+    a, ea, b, eb, d_bits, q_ref, e_ref, ld = exact_dense_ue8m0
+    d, dq, dsf = _ue_outputs((M,), N, ld)
+    dg.dg_fp8_gemm_nt_ue8m0_qout(dev(a), dev(ea), dev(b), dev(eb), d, dq, dsf, workspace=_ws(dg, M, N, K))
+    assert np.array_equal(host(d), d_bits)
+    assert np.array_equal(host(dq), q_ref)
+    assert np.array_equal(host(dsf), e_ref)  # scale padding rows written as 0
+
+
+def test_ue8m0_exact_masked_and_contiguous():
+    dg = require_gpu()
+    g, m_max = 3, 160
+    mm = np.array([150, 0, 77], dtype=np.int32)
+    a, ea = ue8m0.quant_1x128_ue8m0(synth.bf16_grid((g, m_max, K), 861))
+    b, eb = ue8m0.quant_128x128_ue8m0(synth.bf16_grid((g, N, K), 862))
+    sfb = np.stack([ue8m0.sfb_as_fp32(eb[i], N) for i in range(g)])
+    ref, written = gemm.grouped_masked_ref(a, ue8m0.sfa_as_fp32(ea), b, sfb, mm)
+    d_bits = bf16.bits_from_f64(np.where(written[..., None] if written.ndim == 2 else written, ref, 0.0))
+    q_ref, e_ref = ue8m0.quant_1x128_ue8m0(d_bits)
+    d, dq, dsf = _ue_outputs((g, m_max), N, e_ref.shape[-1])
+    dg.dg_grouped_masked_ue8m0_qout(dev(a), dev(ea), dev(b), dev(eb), d, dq, dsf, dev(mm), expected_m=int(mm.mean()),
+                                    workspace=_ws(dg, m_max, N, K, g))
+    d_h, q_h, e_h = host(d), host(dq), host(dsf)
+    for grp in range(g):
+        v = int(mm[grp])
+        assert np.array_equal(d_h[grp, :v], d_bits[grp, :v])
+        assert np.all(d_h[grp, v:] == SENTINEL) and np.all(q_h[grp, v:] == Q_SENT)
+        assert np.array_equal(q_h[grp, :v], q_ref[grp, :v])
+        assert np.array_equal(e_h[grp][:, :v], e_ref[grp][:, :v])
+        assert np.all(e_h[grp][:, v:] == 0xA5)
+
+    mi = synth.contiguous_m_indices([128, 384, 256], [0, 128, 0], [2, 0, 1])
+    m_total = mi.size
+    a, ea = ue8m0.quant_1x128_ue8m0(synth.bf16_grid((m_total, K), 871))
+    b, eb = ue8m0.quant_128x128_ue8m0(synth.bf16_grid((g, N, K), 872))
+    sfb = np.stack([ue8m0.sfb_as_fp32(eb[i], N) for i in range(g)])
+    ref, written = gemm.grouped_contiguous_ref(a, ue8m0.sfa_as_fp32(ea), b, sfb, mi)
+    rows = np.flatnonzero(mi >= 0)
+    d_bits = bf16.bits_from_f64(ref[rows])
+    q_ref, e_ref = ue8m0.quant_1x128_ue8m0(d_bits)
+    d, dq, dsf = _ue_outputs((m_total,), N, m_total)
+    dg.dg_grouped_contiguous_ue8m0_qout(dev(a), dev(ea), dev(b), dev(eb), d, dq, dsf, dev(mi.astype(np.int32)),
+                                        workspace=_ws(dg, m_total, N, K, g))
+    d_h, q_h, e_h = host(d), host(dq), host(dsf)
+    pad = np.flatnonzero(mi < 0)
+    assert np.array_equal(d_h[rows], d_bits)
+    assert np.array_equal(q_h[rows], q_ref)
+    assert np.array_equal(e_h[:, rows], e_ref[:, :rows.size])
+    assert np.all(d_h[pad] == SENTINEL) and np.all(q_h[pad] == Q_SENT) and np.all(e_h[:, pad] == 0xA5)
+
+
+def test_ue8m0_random_inputs():
+    """Random inputs: d within tolerance; every 1x128 tile whose bf16 values
+    equal the oracle's rounding has the oracle's UE8M0 codes and exponent."""
+    dg = require_gpu()
+    m, n, k = 128, 2048, 7168
+    a, ea = ue8m0.quant_1x128_ue8m0(synth.bf16_normal((m, k), 881))
+    b, eb = ue8m0.quant_128x128_ue8m0(synth.bf16_normal((n, k), 882))
+    d64 = gemm.gemm_nt_ref(a, ue8m0.sfa_as_fp32(ea), b, ue8m0.sfb_as_fp32(eb, n))
+    d_bits = bf16.bits_from_f64(d64)
+    q_ref, e_ref = ue8m0.quant_1x128_ue8m0(d_bits)
+    d, dq, dsf = _ue_outputs((m,), n, quant.sf_leading_dim(m))
+    dg.dg_fp8_gemm_nt_ue8m0_qout(dev(a), dev(ea), dev(b), dev(eb), d, dq, dsf, workspace=_ws(dg, m, n, k))
+    d_h, q_h, e_h = host(d), host(dq), host(dsf)
+    check(bf16_to_f64(d_h), d64, "ue8m0 qout random")
+    same = (d_h == d_bits).reshape(m, n // 128, 128).all(axis=2)
+    assert same.sum() >= 100, "too few tiles agree exactly to be a test"
+    q3, qr3 = q_h.reshape(m, n // 128, 128), q_ref.reshape(m, n // 128, 128)
+    assert np.array_equal(q3[same], qr3[same])
+    assert np.array_equal(e_h[:, :m].T[same], e_ref[:, :m].T[same])
