@@ -15,6 +15,14 @@
  * product that is scaled and promoted into an fp32 accumulator; the output is
  * bf16 (round to nearest even).
  *
+ * Entry points, in the order below: the dense NT GEMM and the two MoE grouped
+ * layouts (contiguous, masked); the same with power-of-two (UE8M0) scales;
+ * the forms that also quantise their output for the next layer (fp32 or
+ * UE8M0 output scales); the K-axis grouped weight-gradient GEMM; the dense
+ * GEMM with the NN, TN and TT operand majors (fp32 or UE8M0 scales); the
+ * 1x128 and 128x128 quantisers (row-wise, column-wise for M-major
+ * activations, fp32 or UE8M0 scales); host utilities.
+ *
  * Conventions for every entry point
  *   - All data pointers are DEVICE pointers on the current HIP device; the
  *     caller allocates and owns every buffer (including any workspace).  The

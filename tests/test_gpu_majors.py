@@ -9,6 +9,8 @@ dg_fp8_gemm_nt on the logical operands bit for bit.  Besides that the
 outputs meet the bf16 tolerance rule against the oracle, equal the
 oracle's rounding bit for bit on exact-grid inputs (every scale 2^-8, the
 fp32 result exact in any order), and leave unwritten rows and columns alone.
+The same holds with UE8M0 scales against dg_fp8_gemm_nt_ue8m0, and the
+column quantisers (fp32 and UE8M0 scales) match the oracle bit for bit.
 """
 
 import numpy as np
