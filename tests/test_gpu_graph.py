@@ -32,9 +32,10 @@ def _bufs(dg, m, n, k, groups=None):
     return x, a, sfa, b, sfb, ws
 
 
-def test_dense_stream_k_graph_replays():
+@pytest.mark.parametrize("m,n,k", [(128, 7168, 16384),   # 4 K parts per 128x128 tile
+                                   (128, 4096, 7168)])   # 4 K parts per 64x64 tile, two workgroups per CU
+def test_dense_stream_k_graph_replays(m, n, k):
     dg = require_gpu()
-    m, n, k = 128, 7168, 16384  # 4 K parts per 128x128 tile
     cfg = dict(kv.split("=") for kv in dg.dg_describe_config(0, m, n, k, 1, dg.dg_get_num_cus()).split())
     assert int(cfg["stream_k"]) == 1
     x, a, sfa, b, sfb, ws = _bufs(dg, m, n, k)
