@@ -43,6 +43,9 @@
  *   - a, b, d, sfa, sfb 16-byte aligned; lda, ldb multiples of 16 (bytes =
  *     elements); ldd a multiple of 8 elements; ld_sfa a multiple of 4 and
  *     >= the rows it covers (DG_ERR_MISALIGNED / DG_ERR_INVALID_VALUE).
+ *   - Each operand (per group) stays below 4 GiB, and the output holds fewer
+ *     than 2^31 tiles of 64x64 (over all groups of the masked and K-grouped
+ *     layouts): DG_ERR_UNSUPPORTED_SHAPE otherwise.
  */
 #ifndef DG_H_
 #define DG_H_
@@ -362,7 +365,9 @@ int dg_quant_1x128_mn_ue8m0(const uint16_t* x, uint8_t* q, uint8_t* sf, int rows
  * The workspace holds split-K partial sums and per-tile arrival counters.  It
  * must be zero-filled once before its first use; every call leaves it ready
  * for the next one (counters back at zero), so it can be reused without
- * clearing.  Calls that run at the same time must not share a workspace. */
+ * clearing.  Calls that run at the same time must not share a workspace.
+ * Shapes the GEMMs reject for their tile count (see the shape rules above)
+ * report 0. */
 size_t dg_get_workspace_size(int m, int n, int k, int num_groups);
 
 /* Number of compute units the persistent kernels are sized to (set_num_sms /
@@ -394,7 +399,8 @@ const char* dg_get_last_error_string(void);
  * the *_qout entry points; m is M, M_total or M_max; expected_m is the masked
  * layout's hint, 0 otherwise),
  * written into buf (NUL-terminated, truncated to len).  Returns DG_SUCCESS or
- * an error for invalid arguments.  Pure host logic: needs no device. */
+ * an error for invalid arguments or shapes the GEMMs reject for their tile
+ * count.  Pure host logic: needs no device. */
 int dg_describe_config(int layout, int m, int n, int k, int num_groups, int expected_m,
                        int num_cus, char* buf, size_t len);
 

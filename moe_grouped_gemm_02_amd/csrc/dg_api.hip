@@ -33,6 +33,13 @@ int ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// count * stride * elem < lim, for count, stride >= 0 and elem, lim > 0,
+// decided without forming the product (strides come from the caller).
+bool below(int64_t count, int64_t stride, int64_t elem, int64_t lim) {
+  if (count == 0 || stride == 0) return true;
+  return stride <= (lim - 1) / elem / count;
+}
+
 int env_num_cus() {
   const char* s = getenv("DG_NUM_CUS");
   if (!s || !*s) return 0;
@@ -89,7 +96,7 @@ int check_gemm_common(const uint8_t* a, const void* sfa, const uint8_t* b, const
   if (ld_sfa % 4) return fail(DG_ERR_MISALIGNED, "ld_sfa must be a multiple of 4");
   // The kernels address each operand (per group) with 32-bit byte offsets.
   const int64_t lim = (int64_t)1 << 32;
-  if ((int64_t)rows * lda >= lim || (int64_t)n * ldb >= lim || (int64_t)(k / 128) * ld_sfa * 4 >= lim)
+  if (!below(rows, lda, 1, lim) || !below(n, ldb, 1, lim) || !below(k / 128, ld_sfa, 4, lim))
     return fail(DG_ERR_UNSUPPORTED_SHAPE, "operand of 4 GiB or more (per group)");
   return DG_SUCCESS;
 }
@@ -106,6 +113,8 @@ int check_workspace(const dg::GemmConfig& cfg, int layout, int rows, int n, int 
 
 int run_gemm(int layout, dg::GemmParams& p, int rows, int groups, void* ws, size_t ws_bytes,
              void* stream, int expected_m = 0) {
+  if (!dg::plannable(layout, rows, p.n, groups))
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many output tiles (m=%d n=%d groups=%d)", rows, p.n, groups);
   const int cus = resolve_num_cus();
   if (cus < 0) return fail(DG_ERR_HIP, "cannot query the device's compute-unit count");
   const bool qout = p.dq != nullptr;
@@ -148,7 +157,9 @@ int check_qout(const QOut* q, int rows, int n, int groups) {
   if (n % 128) return fail(DG_ERR_UNSUPPORTED_SHAPE, "n=%d is not a multiple of 128 (quantised output)", n);
   if (q->ld_dsf < rows || q->ld_dsf < 4) return fail(DG_ERR_INVALID_VALUE, "ld_dsf smaller than the rows or 4");
   if (q->ld_dsf % 4) return fail(DG_ERR_MISALIGNED, "ld_dsf must be a multiple of 4");
-  if ((int64_t)groups * rows * n >= ((int64_t)1 << 40)) return fail(DG_ERR_UNSUPPORTED_SHAPE, "quantised output too large");
+  if ((int64_t)rows * n > (((int64_t)1 << 40) - 1) / groups) return fail(DG_ERR_UNSUPPORTED_SHAPE, "quantised output too large");
+  if (!below((int64_t)groups * (n / 128), q->ld_dsf, 4, (int64_t)1 << 40))
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "output scales too large");
   return DG_SUCCESS;
 }
 
@@ -168,8 +179,8 @@ void set_scales(dg::GemmParams& p, const void* sfa, const void* sfb, int n, int 
   p.sfa = static_cast<const float*>(sfa);
   p.sfb = static_cast<const float*>(sfb);
   p.sf_ue8m0 = ue8m0 ? 1 : 0;
-  p.ld_sfb = ue8m0 ? (((int64_t)(n + 127) / 128 + 3) / 4 * 4) : 0;
-  p.sfb_gstride = ue8m0 ? (int64_t)(k / 128) * p.ld_sfb : (int64_t)((n + 127) / 128) * (k / 128);
+  p.ld_sfb = ue8m0 ? ((((int64_t)n + 127) / 128 + 3) / 4 * 4) : 0;
+  p.sfb_gstride = ue8m0 ? (int64_t)(k / 128) * p.ld_sfb : (((int64_t)n + 127) / 128) * (k / 128);
 }
 
 int gemm_nt_impl(const uint8_t* a, const void* sfa, const uint8_t* b, const void* sfb, uint16_t* d,
@@ -205,13 +216,13 @@ int gemm_majors_impl(int majors, const uint8_t* a, const void* sfa, const uint8_
     if (m % 16) return fail(DG_ERR_UNSUPPORTED_SHAPE, "m=%d is not a multiple of 16 (M-major A)", m);
     if (lda < m) return fail(DG_ERR_INVALID_VALUE, "lda smaller than m (M-major A)");
     if (lda % 16) return fail(DG_ERR_MISALIGNED, "lda must be a multiple of 16 bytes");
-    if ((int64_t)k * lda >= lim) return fail(DG_ERR_UNSUPPORTED_SHAPE, "operand of 4 GiB or more");
+    if (!below(k, lda, 1, lim)) return fail(DG_ERR_UNSUPPORTED_SHAPE, "operand of 4 GiB or more");
   }
   if (bt) {
     if (n % 16) return fail(DG_ERR_UNSUPPORTED_SHAPE, "n=%d is not a multiple of 16 (N-major B)", n);
     if (ldb < n) return fail(DG_ERR_INVALID_VALUE, "ldb smaller than n (N-major B)");
     if (ldb % 16) return fail(DG_ERR_MISALIGNED, "ldb must be a multiple of 16 bytes");
-    if ((int64_t)k * ldb >= lim) return fail(DG_ERR_UNSUPPORTED_SHAPE, "operand of 4 GiB or more");
+    if (!below(k, ldb, 1, lim)) return fail(DG_ERR_UNSUPPORTED_SHAPE, "operand of 4 GiB or more");
   }
   if (m == 0 || n == 0) return ok();
   dg::GemmParams p{};
@@ -281,8 +292,8 @@ int k_grouped_impl(const uint8_t* a, const float* sfa, const uint8_t* b, const f
   if (n % 8) return fail(DG_ERR_MISALIGNED, "n must be a multiple of 8 (rows of d are packed)");
   if (ld_sfb < n || ld_sfb < 4) return fail(DG_ERR_INVALID_VALUE, "ld_sfb=%lld smaller than n (%d) or 4", (long long)ld_sfb, n);
   if (ld_sfb % 4) return fail(DG_ERR_MISALIGNED, "ld_sfb must be a multiple of 4");
-  if ((int64_t)(k / 128) * ld_sfb * 4 >= ((int64_t)1 << 32)) return fail(DG_ERR_UNSUPPORTED_SHAPE, "sfb of 4 GiB or more");
-  if ((int64_t)num_groups * ((m + 63) / 64) * ((n + 63) / 64) >= ((int64_t)1 << 31))
+  if (!below(k / 128, ld_sfb, 4, (int64_t)1 << 32)) return fail(DG_ERR_UNSUPPORTED_SHAPE, "sfb of 4 GiB or more");
+  if ((((int64_t)m + 63) / 64) * (((int64_t)n + 63) / 64) > (((int64_t)1 << 31) - 1) / num_groups)
     return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many output tiles");
   if (m == 0 || n == 0) return ok();
   dg::GemmParams p{};
@@ -332,7 +343,7 @@ int quant_128x128_impl(const uint16_t* w, uint8_t* q, void* sf, int rows, int co
   if (cols % 128) return fail(DG_ERR_UNSUPPORTED_SHAPE, "cols=%d is not a multiple of 128", cols);
   if (!w || !q || !sf) return fail(DG_ERR_INVALID_VALUE, "null pointer argument");
   if (!aligned16(w) || !aligned16(q) || !aligned16(sf)) return fail(DG_ERR_MISALIGNED, "w, q and sf must be 16-byte aligned");
-  if (num_groups > 65535 || (rows + 127) / 128 > 65535) return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many blocks");
+  if (num_groups > 65535 || rows > 65535 * 128) return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many blocks");
   if (rows == 0 || cols == 0) return ok();
   const hipError_t e = dg::launch_quant_128x128(w, q, sf, rows, cols, num_groups, pow2,
                                                 static_cast<hipStream_t>(stream));
@@ -529,7 +540,7 @@ int dg_quant_128x128_ue8m0(const uint16_t* w, uint8_t* q, uint8_t* sf, int rows,
 
 int64_t dg_get_ue8m0_sfb_leading_dim(int n) {
   if (n < 0) return -1;
-  return ((int64_t)(n + 127) / 128 + 3) / 4 * 4;
+  return (((int64_t)n + 127) / 128 + 3) / 4 * 4;
 }
 
 size_t dg_get_workspace_size(int m, int n, int k, int num_groups) {
@@ -544,7 +555,7 @@ size_t dg_get_workspace_size(int m, int n, int k, int num_groups) {
   for (int qout = 0; qout <= 1; ++qout)
     for (int layout = dg::kDense; layout <= dg::kMasked; ++layout)
       for (int h : hints) {
-        if (h && layout != dg::kMasked) break;
+        if ((h && layout != dg::kMasked) || !dg::plannable(layout, m, n, num_groups)) break;
         const dg::GemmConfig c = dg::choose_config(layout, m, n, k, num_groups, cus, h, qout != 0);
         const size_t need = dg::workspace_bytes_for(c, layout, m, n, num_groups);
         if (need > worst) worst = need;
@@ -580,6 +591,8 @@ int dg_describe_config(int layout, int m, int n, int k, int num_groups, int expe
   if (layout < dg::kDense || layout > dg::kKGrouped || m < 0 || n < 0 || k < 0 ||
       num_groups < 1 || expected_m < 0 || num_cus < 1 || !buf || len == 0)
     return fail(DG_ERR_INVALID_VALUE, "bad arguments to dg_describe_config");
+  if (!dg::plannable(layout, m, n, num_groups))
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many output tiles (m=%d n=%d groups=%d)", m, n, num_groups);
   const dg::GemmConfig c = dg::choose_config(layout, m, n, k, num_groups, num_cus, expected_m, qout);
   snprintf(buf, len, "layout=%s bm=%d bn=%d stream_k=%d sk_split=%d grid=%d tiles=%d variant=%d k_rotate=%d workspace=%zu",
            layout_name(layout), c.bm, c.bn, c.stream_k, c.sk_split, c.grid, c.tiles, c.variant, c.k_rotate,

@@ -1144,7 +1144,15 @@ hipError_t launch_kgrouped(const GemmParams& p, const Schedule& s, int grid, hip
   return hipGetLastError();
 }
 
-int cdiv(int a, int b) { return (a + b - 1) / b; }
+// Ceiling division of a >= 0 by b > 0 that cannot overflow.
+int cdiv(int a, int b) { return a / b + (a % b != 0); }
+int64_t cdiv64(int64_t a, int64_t b) { return a / b + (a % b != 0); }
+
+constexpr int smallest_tile_dim(bool rows) {
+  int v = 1 << 30;
+  for (const Variant& t : kVariants) v = std::min(v, rows ? t.bm : t.bn);
+  return v;
+}
 
 // Stream-K partial slots are addressed with 32-bit offsets: 2 * grid slots of
 // at most 256 KB stay below 2^31 bytes with this cap.
@@ -1177,6 +1185,13 @@ int forced_rotate() {  // third field: 0 or 1, -1 when absent
 
 }  // namespace
 
+bool plannable(int layout, int m, int n, int groups) {
+  if (m < 0 || n < 0 || groups < 1) return false;
+  const int64_t gmul = (layout == kMasked || layout == kKGrouped) ? groups : 1;
+  const int64_t tiles = cdiv64(m, smallest_tile_dim(true)) * cdiv64(n, smallest_tile_dim(false));  // < 2^50
+  return tiles <= ((1LL << 31) - 1) / gmul;
+}
+
 bool variant_quantises_output(int variant) {
   return variant >= 0 && variant < kNumVariants && kVariants[variant].bn % 128 == 0;
 }
@@ -1191,12 +1206,14 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
   const bool hinted = layout == kMasked && expected_m > 0 && expected_m < m;
   const int rows = hinted ? expected_m : m;
   const int gmul = (layout == kMasked || layout == kKGrouped) ? groups : 1;
-  auto tiles_of = [&](int bm, int bn) { return cdiv(rows, bm) * gmul * cdiv(n, bn); };
+  // Tile counts in 64 bits: with plannable() shapes every count fits an int,
+  // but the products below (10 x tiles, tiles x parts) need not.
+  auto tiles_of = [&](int bm, int bn) { return (int64_t)cdiv(rows, bm) * gmul * cdiv(n, bn); };
   int v;
   if (rows <= 128) {
     // Decode-sized M: the launch streams B once.  128x128 tiles (8 waves)
     // when they alone keep most CUs busy or K is long, else 64x64 tiles.
-    const int t128 = tiles_of(128, 128);
+    const int64_t t128 = tiles_of(128, 128);
     v = (rows > 64 && (10 * t128 >= 7 * num_cus || nkb >= 64)) ? 6 : 4;
   } else if (tiles_of(256, 256) >= num_cus / 2) {
     v = 0;
@@ -1205,7 +1222,7 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
     // unless 128 columns fill the CUs' last round better (measured on the
     // pages' all-valid masked rows: 1024x7168x2048 39.8 -> 31.1 us with
     // 128x256, 1024x4096x7168 58.5 -> 53.1 us with 128x128).
-    auto fill = [&](int t) { return (double)t / (double)(cdiv(t, num_cus) * num_cus); };
+    auto fill = [&](int64_t t) { return (double)t / (double)(cdiv64(t, num_cus) * num_cus); };
     v = fill(tiles_of(128, 256)) >= fill(tiles_of(128, 128)) ? 5 : 6;
   }
   // A quantised output needs whole 128-column blocks per tile: the 64-wide
@@ -1225,7 +1242,7 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
   // decode-sized tiles into S equal parts (one part per workgroup), larger
   // tiles with long K into equal runs of iterations over all CUs.  The
   // estimate uses the hinted rows for the masked layout.
-  const int est = tiles_of(c.bm, c.bn);
+  const int64_t est = tiles_of(c.bm, c.bn);
   int sk = 0;  // 0: data-parallel, 1: equal runs, S >= 2: S parts per tile
   if (layout != kContiguous && layout != kKGrouped && nkb >= 2 && 10 * est < 7 * num_cus) {
     // K parts for 128-row (or smaller) tiles up to 1024 rows in all; beyond
@@ -1235,19 +1252,19 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
       // (quantised output): fewer tiles, so more parts (64x4096x7168 fused:
       // 27.5 -> 24.2 us with 8 parts instead of 3).
       const int min_slices = (c.bm * c.bn >= 128 * 128 && !widened) ? 16 : 8;
-      int parts = std::min(num_cus / std::max(est, 1), nkb / min_slices);
+      int parts = (int)std::min<int64_t>(num_cus / std::max<int64_t>(est, 1), nkb / min_slices);
       // Two 64x64 workgroups share a CU: at least 4 parts where 2 x CUs hold
       // them (128x4096x7168: 20.4 -> 19.5 us with 4 parts on 512 workgroups
       // instead of 2 on 256; 64x7168x16384: 36.8 -> 33.8 us).
       if (v == 4 || v == 7)
-        parts = std::max(parts, std::min({4, 2 * num_cus / std::max(est, 1), nkb / min_slices}));
+        parts = std::max(parts, (int)std::min<int64_t>({4, 2 * num_cus / std::max<int64_t>(est, 1), nkb / min_slices}));
       if (c.bm * c.bn < 128 * 128) parts = std::min(parts, 6);  // 64x2112x7168: 6 parts 3% faster than 4
       // A fixup costs a few microseconds; short K ranges are not worth
       // cutting (64x7168x2048: 11.6 us in 2 parts, 10.2 us whole).
       if (nkb < 24) parts = 1;
       if (parts >= 2) sk = parts;
     }
-    if (sk == 0 && rows > 128 && (int64_t)est * nkb >= 24LL * num_cus) sk = 1;
+    if (sk == 0 && rows > 128 && est * nkb >= 24LL * num_cus) sk = 1;
   }
   const int fs = forced_stream_k();
   if (fs >= 0) sk = fs;
@@ -1263,13 +1280,14 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
   // The same holds for their K parts.
   const int per_cu = (v == 4 || v == 7) ? 2 : 1;
   const int cap = std::min(num_cus * per_cu, kMaxStreamKGrid);
+  const int64_t slots = c.sk_split ? (int64_t)c.tiles * c.sk_split : cap;
   c.grid = !c.stream_k ? std::max(1, std::min(c.tiles, num_cus * per_cu))
-           : (c.sk_split ? std::min(cap, cdiv(c.tiles * c.sk_split, 8) * 8) : cap);
-  c.sk_slots = c.sk_split ? c.tiles * c.sk_split : c.grid;
-  if (c.stream_k && (int64_t)2 * c.sk_slots * c.bm * c.bn * 4 >= (1LL << 31)) {
-    c.stream_k = c.sk_split = c.sk_slots = 0;  // partial slots must stay 32-bit addressable
+           : (int)std::min<int64_t>(cap, cdiv64(slots, 8) * 8);
+  if (c.stream_k && 2 * slots * c.bm * c.bn * 4 >= (1LL << 31)) {
+    c.stream_k = c.sk_split = 0;  // partial slots must stay 32-bit addressable
     c.grid = std::max(1, std::min(c.tiles, num_cus));
   }
+  c.sk_slots = c.stream_k ? (int)slots : 0;
   c.group_m = 8;
   // Rotated K walks for the decode-sized tiles when the weight rows are a
   // multiple of 16 KiB apart (see the kernel's K walk).  The 256x256 tile

@@ -85,6 +85,10 @@ struct Schedule {
   int k_rotate;      // see GemmConfig
 };
 
+// Whether choose_config() may be asked about this shape: the output tile
+// count at the smallest tile variant (times the groups of the masked and
+// K-grouped layouts) is below 2^31.  Its precondition; every caller checks.
+bool plannable(int layout, int m, int n, int groups);
 // expected_m (masked layout only, 0 = unknown): typical valid rows per group,
 // used to pick the tile shape.
 // qout: the call also quantises its output, which needs tiles whose columns

@@ -256,7 +256,7 @@ hipError_t launch_quant_1x128(const uint16_t* x, uint8_t* q, void* sf, int rows,
 
 hipError_t launch_quant_1x128_mn(const uint16_t* x, uint8_t* q, void* sf, int rows, int cols,
                                  int64_t ld_sf, bool pow2, hipStream_t stream) {
-  const dim3 grid((cols + 255) / 256, rows / kBlockK);
+  const dim3 grid(cols / 256 + (cols % 256 != 0), rows / kBlockK);
   if (pow2)
     hipLaunchKernelGGL(quant_1x128_mn_kernel<true>, grid, dim3(256), 0, stream, x, q, sf, rows, cols, ld_sf);
   else

@@ -215,3 +215,26 @@ def test_column_quantiser_argument_errors():
     assert lib.dg_quant_1x128_mn(P(FAKE), P(FAKE), P(FAKE), 128, 64, 66, None) == -3   # ld_sf % 4
     assert lib.dg_quant_1x128_mn(None, P(FAKE), P(FAKE), 128, 64, 64, None) == -1
     assert lib.dg_quant_1x128_mn(P(FAKE), P(FAKE), P(FAKE), 0, 64, 64, None) == 0      # nothing to do
+
+
+def test_tile_count_limit():
+    # Output tile counts (at 64x64) of 2^31 or more are refused before any
+    # planning; the workspace query reports 0 for them.
+    big = 2**31 - 1
+    assert _gemm(m=1 << 24, n=1 << 24, k=0, lda=0, ldb=0, ldd=1 << 24, ld_sfa=1 << 24) == -2
+    assert "too many output tiles" in dg.dg_get_last_error_string()
+    with pytest.raises(dg.DGError):
+        dg.dg_describe_config(dg.LAYOUT_DENSE, big, big, 128, 1, 256)
+    with pytest.raises(dg.DGError):
+        dg.dg_describe_config(dg.LAYOUT_MASKED, 1 << 16, 1 << 16, 128, 4096, 256)
+    assert dg.dg_get_workspace_size(big, big, 1 << 20, 1) == 0
+    # Just below the limit the planner still answers.
+    fields = dict(kv.split("=") for kv in dg.dg_describe_config(dg.LAYOUT_DENSE, 1 << 20, 1 << 17, 128, 1, 256).split())
+    assert int(fields["tiles"]) > 0
+
+
+def test_huge_leading_dimensions_are_refused():
+    assert _gemm(lda=1 << 62) == -2
+    assert _gemm(ld_sfa=1 << 62) == -2
+    assert _gemm_qout(ld_dsf=1 << 62) == -2
+    assert dg.dg_get_ue8m0_sfb_leading_dim(2**31 - 1) == ((2**31 - 1 + 127) // 128 + 3) // 4 * 4
