@@ -238,3 +238,25 @@ def test_huge_leading_dimensions_are_refused():
     assert _gemm(ld_sfa=1 << 62) == -2
     assert _gemm_qout(ld_dsf=1 << 62) == -2
     assert dg.dg_get_ue8m0_sfb_leading_dim(2**31 - 1) == ((2**31 - 1 + 127) // 128 + 3) // 4 * 4
+
+
+def test_quantiser_grid_limits():
+    # 65535 row blocks of 128x128 weights and 65535 K blocks of an M-major
+    # activation are the largest grids accepted; one more row is refused.
+    # (The accepted calls reach the launch, which fails without a GPU.)
+    lib = dg.raw()
+    P = ctypes.c_void_p
+    assert lib.dg_quant_128x128(P(FAKE), P(FAKE), P(FAKE), 65535 * 128 + 1, 128, 1, None) == -2
+    assert lib.dg_quant_128x128(P(FAKE), P(FAKE), P(FAKE), 128, 128, 65536, None) == -2
+    assert lib.dg_quant_1x128_mn(P(FAKE), P(FAKE), P(FAKE), 65536 * 128, 8, ctypes.c_int64(8), None) == -2
+    if not _has_gpu():
+        assert lib.dg_quant_128x128(P(FAKE), P(FAKE), P(FAKE), 65535 * 128, 128, 1, None) == -5
+        assert lib.dg_quant_1x128_mn(P(FAKE), P(FAKE), P(FAKE), 65535 * 128, 8, ctypes.c_int64(8), None) == -5
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False

@@ -1,4 +1,5 @@
-"""Operands at the size limit of the kernels' 32-bit byte offsets.
+"""Operands at the size limit of the kernels' 32-bit byte offsets, and the
+quantisers at the largest grids the host accepts.
 
 Each e4m3 operand (per group) must stay below 4 GiB; the host rejects larger
 ones.  These tests run operands just under that limit, so the last rows of A
@@ -15,7 +16,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import majors
+from oracle import majors, quant
 from tests.gpu_util import SENTINEL, bf16_to_f64, host, require_gpu
 from tests.tolerance import check
 
@@ -109,3 +110,44 @@ def test_m_major_activation_just_under_4gib():
     torch.cuda.empty_cache()
     ref = majors.gemm_layout_ref("tn", a_cols, sa_rows, host(b_s), host(sfb))
     check(bf16_to_f64(host(d)[rows]), ref, "M-major A just under 4 GiB")
+
+
+def _bf16_normal(shape, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    return torch.randn(shape, device="cuda", generator=g).to(torch.bfloat16).view(torch.int16)
+
+
+def test_weight_quantiser_at_the_block_limit():
+    """128x128 blocks: 65535 row blocks (the host's limit), the last one half
+    full; sampled blocks, the first and last included, bit for bit."""
+    dg = require_gpu()
+    rows, cols = 65535 * 128 - 64, 128
+    w = _bf16_normal((rows, cols), 2301)
+    q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    sf = torch.full((65535, 1), float("nan"), dtype=torch.float32, device="cuda")
+    dg.dg_quant_128x128(w, q, sf)
+    torch.cuda.synchronize()
+    sf_h = host(sf)
+    for blk in _sample(65535, 6, 2302):
+        r0, r1 = 128 * blk, min(128 * blk + 128, rows)
+        rq, rsf = quant.quant_128x128(host(w[r0:r1]))
+        assert np.array_equal(host(q[r0:r1]), rq), f"codes of block {blk}"
+        assert sf_h[blk, 0].view(np.uint32) == rsf[0, 0].view(np.uint32), f"scale of block {blk}"
+
+
+def test_column_quantiser_at_the_k_block_limit():
+    """M-major activations with K = 65535 x 128 (the host's limit on K
+    blocks), M = 8: sampled K blocks, the first and last included, bit for bit."""
+    dg = require_gpu()
+    k, m = 65535 * 128, 8
+    x = _bf16_normal((k, m), 2311)
+    q = torch.empty((k, m), dtype=torch.uint8, device="cuda")
+    ld = dg.dg_get_sf_leading_dim(m)
+    sf = torch.full((k // 128, ld), float("nan"), dtype=torch.float32, device="cuda")
+    dg.dg_quant_1x128_mn(x, q, sf)
+    torch.cuda.synchronize()
+    sf_h = host(sf)
+    for kb in _sample(k // 128, 6, 2312):
+        rq, rsf = majors.quant_1x128_mn(host(x[128 * kb:128 * kb + 128]), ld_sf=ld)
+        assert np.array_equal(host(q[128 * kb:128 * kb + 128]), rq), f"codes of K block {kb}"
+        assert np.array_equal(sf_h[kb].view(np.uint32), rsf[0].view(np.uint32)), f"scales of K block {kb}"
