@@ -3,8 +3,10 @@ memset): a captured quantise + GEMM sequence, replayed several times with
 eager work and synchronisations in between, must give the eager result bit
 for bit on every replay.  Covered: the dense decode shape with stream-K K
 parts (the arrival counters are reset inside the kernel, so the workspace
-serves every replay), and the masked layout whose valid-row counts change
-between replays on the device, as in graph-captured MoE decode."""
+serves every replay), the masked layout whose valid-row counts change
+between replays on the device, as in graph-captured MoE decode, and one
+graph holding the contiguous layout with a quantised output (padding rows
+included) and the K-grouped GEMM (an empty group included)."""
 
 import numpy as np
 import pytest
@@ -103,3 +105,69 @@ def test_masked_graph_replays_with_changing_counts():
             g.replay()
             torch.cuda.synchronize()
             assert torch.equal(d.view(torch.int16), want.view(torch.int16)), f"counts {c.tolist()} pass {rep}"
+
+
+def test_contiguous_qout_and_k_grouped_graph_replays():
+    dg = require_gpu()
+    # Contiguous with a quantised output: 4 row blocks of 128 owned by groups
+    # 2, 0, padding (-1) and 3 of 4 experts.
+    groups, m_total, n, k = 4, 512, 1024, 1024
+    x = dev(synth.bf16_normal((m_total, k), 961))
+    w = dev(synth.bf16_normal((groups, n, k), 962))
+    a = torch.empty((m_total, k), dtype=torch.uint8, device="cuda")
+    sfa = torch.empty((k // 128, dg.dg_get_sf_leading_dim(m_total)), dtype=torch.float32, device="cuda")
+    b = torch.empty((groups, n, k), dtype=torch.uint8, device="cuda")
+    sfb = torch.empty((groups, n // 128, k // 128), dtype=torch.float32, device="cuda")
+    dg.dg_quant_128x128(w, b, sfb)
+    ids = torch.from_numpy(np.repeat(np.array([2, 0, -1, 3], dtype=np.int32), 128)).cuda()
+    d = torch.empty((m_total, n), dtype=torch.bfloat16, device="cuda")
+    dq = torch.empty((m_total, n), dtype=torch.uint8, device="cuda")
+    dsf = torch.empty((n // 128, dg.dg_get_sf_leading_dim(m_total)), dtype=torch.float32, device="cuda")
+    # K-grouped: 3 groups over K = 2048 with offsets 0, 512, 512, 2048.
+    m2, n2, k2 = 256, 512, 2048
+    x2 = dev(synth.bf16_normal((m2, k2), 963))
+    y2 = dev(synth.bf16_normal((n2, k2), 964))
+    a2 = torch.empty((m2, k2), dtype=torch.uint8, device="cuda")
+    sfa2 = torch.empty((k2 // 128, dg.dg_get_sf_leading_dim(m2)), dtype=torch.float32, device="cuda")
+    b2 = torch.empty((n2, k2), dtype=torch.uint8, device="cuda")
+    sfb2 = torch.empty((k2 // 128, dg.dg_get_sf_leading_dim(n2)), dtype=torch.float32, device="cuda")
+    offs = torch.tensor([0, 512, 512, 2048], dtype=torch.int32, device="cuda")
+    d2 = torch.empty((3, m2, n2), dtype=torch.bfloat16, device="cuda")
+    outs = (d, dq, dsf, d2)
+
+    def step():
+        dg.dg_quant_1x128(x, a, sfa)
+        dg.dg_grouped_contiguous_qout(a, sfa, b, sfb, d, dq, dsf, ids)
+        dg.dg_quant_1x128(x2, a2, sfa2)
+        dg.dg_quant_1x128(y2, b2, sfb2)
+        dg.dg_k_grouped_nt(a2, sfa2, b2, sfb2, d2, offs)
+
+    def clear():
+        for t in outs:
+            t.view(torch.uint8).fill_(0)
+
+    clear()
+    step()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        clear()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, t, want in zip(("d", "dq", "dsf", "d2"), outs, eager):
+            assert torch.equal(t.view(torch.uint8), want.view(torch.uint8)), f"{name} differs on replay {r}"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+    # The padding block stays untouched and the empty K group is zero.
+    assert not torch.any(d[256:384].view(torch.int16)) and not torch.any(dq[256:384])
+    assert not torch.any(d2[1].view(torch.int16))
