@@ -6,7 +6,8 @@ parts (the arrival counters are reset inside the kernel, so the workspace
 serves every replay), the masked layout whose valid-row counts change
 between replays on the device, as in graph-captured MoE decode, and one
 graph holding the contiguous layout with a quantised output (padding rows
-included) and the K-grouped GEMM (an empty group included)."""
+included) and the K-grouped GEMM (an empty group included), and the UE8M0
+column quantiser followed by the TN GEMM in K parts."""
 
 import numpy as np
 import pytest
@@ -171,3 +172,48 @@ def test_contiguous_qout_and_k_grouped_graph_replays():
     # The padding block stays untouched and the empty K group is zero.
     assert not torch.any(d[256:384].view(torch.int16)) and not torch.any(dq[256:384])
     assert not torch.any(d2[1].view(torch.int16))
+
+
+def test_tn_ue8m0_graph_replays():
+    """M-major activations quantised with exponent-byte scales by the column
+    quantiser, then the TN GEMM in K parts (decode shape), in one graph."""
+    dg = require_gpu()
+    m, n, k = 128, 4096, 7168
+    cfg = dict(kv.split("=") for kv in dg.dg_describe_config(0, m, n, k, 1, dg.dg_get_num_cus()).split())
+    assert int(cfg["stream_k"]) == 1
+    x_t = dev(synth.bf16_normal((k, m), 971))          # activations stored [K][M]
+    w = dev(synth.bf16_normal((n, k), 972))
+    a_t = torch.empty((k, m), dtype=torch.uint8, device="cuda")
+    ea = torch.empty((k // 128, dg.dg_get_sf_leading_dim(m)), dtype=torch.uint8, device="cuda")
+    b = torch.empty((n, k), dtype=torch.uint8, device="cuda")
+    eb = torch.empty((k // 128, dg.dg_get_ue8m0_sfb_leading_dim(n)), dtype=torch.uint8, device="cuda")
+    dg.dg_quant_128x128_ue8m0(w, b, eb)
+    b_t = b.t().contiguous()                           # weights stored [K][N]
+    ws_bytes = dg.dg_get_workspace_size(m, n, k, 1)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
+    d = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        dg.dg_quant_1x128_mn_ue8m0(x_t, a_t, ea)
+        dg.dg_fp8_gemm_tn_ue8m0(a_t, ea, b_t, eb, d, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = d.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        d.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d.view(torch.int16), eager.view(torch.int16)), f"replay {r}"
+        step()
+        torch.cuda.synchronize()
