@@ -35,8 +35,13 @@ def remarks(src):
         res = subprocess.run(cmd, capture_output=True, text=True, cwd=tmp)
     if res.returncode != 0:
         raise RuntimeError(res.stderr[-4000:])
+    return parse(res.stderr)
+
+
+def parse(text):
+    """{mangled kernel name: {remark field: value}} from the remark lines."""
     kernels, cur = {}, None
-    for line in res.stderr.splitlines():
+    for line in text.splitlines():
         m = re.search(r"remark: Function Name: (\S+)", line)
         if m:
             cur = kernels.setdefault(m.group(1), {})
