@@ -186,6 +186,15 @@ def drive_planning(lib):
                         call(lib.dg_get_workspace_size, [m, n, k, groups])
     for v in (-1, 4097):
         check_status(lib, call(lib.dg_set_num_cus, [v]), f"set_num_cus {v}")
+    # Forced configurations, well-formed or not ("variant:division:k_rotate").
+    buf = ctypes.create_string_buffer(256)
+    for forced in ("0", "6:4:1", "4:2", "99", "-1", "0:9999", "4:abc:7", ":", "::", "5:1:", "10:0:0", "3:-5"):
+        os.environ["DG_FORCE_CONFIG"] = forced
+        for layout, m, n, k, g in ((0, 128, 7168, 16384, 1), (2, 256, 4096, 7168, 8), (1, 1024, 4096, 7168, 4),
+                                   (8, 64, 2048, 7168, 1), (3, 256, 512, 4096, 4), (0, 1, 1, 128, 1)):
+            check_status(lib, call(lib.dg_describe_config, [layout, m, n, k, g, 0, 256, buf, 256]), f"forced {forced}")
+            call(lib.dg_get_workspace_size, [m, n, k, g])
+    os.environ.pop("DG_FORCE_CONFIG")
     for v in (-2**31, -1, 0, 1, 5, 2**31 - 1):
         call(lib.dg_get_sf_leading_dim, [v])
         call(lib.dg_get_ue8m0_sfb_leading_dim, [v])
