@@ -362,10 +362,13 @@ int dg_quant_1x128_mn_ue8m0(const uint16_t* x, uint8_t* q, uint8_t* sf, int rows
 
 /* Workspace bytes a GEMM of this shape needs (0 when it needs none).  For the
  * masked layout pass m = m_max; for contiguous pass m = m_total.
- * The workspace holds split-K partial sums and per-tile arrival counters.  It
- * must be zero-filled once before its first use; every call leaves it ready
- * for the next one (counters back at zero), so it can be reused without
- * clearing.  Calls that run at the same time must not share a workspace.
+ * The workspace holds per-tile arrival counters in a region of fixed size at
+ * its start (32 KiB, the same for every shape and configuration) and the
+ * split-K partial sums after it.  It must be zero-filled once before its
+ * first use; every call leaves the counters back at zero, so a workspace can
+ * be reused without clearing by later calls of any shape, as long as it is
+ * large enough for each.  Calls that run at the same time must not share a
+ * workspace.
  * Shapes the GEMMs reject for their tile count (see the shape rules above)
  * report 0. */
 size_t dg_get_workspace_size(int m, int n, int k, int num_groups);

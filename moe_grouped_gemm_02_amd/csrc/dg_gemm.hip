@@ -846,9 +846,13 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
         // way.  (On 64x64 tiles the counter read costs as much as the 16 KB
         // store it can save: measured 2-3% slower there.)
         constexpr bool kEarly = kFrag <= 8 && T::kWaves <= 8 && T::BM * T::BN >= 128 * 128;
+        // The partial slots follow the counter region of the workspace.  A
+        // run of S parts per tile has one segment and one slot; an equal run
+        // may end in one tile and begin in the next, so it has two.
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            uniform_ptr(p.workspace), (short)0, 2 * s.sk_slots * kPartBytes, 0x00020000);
-        const int my_slot = 2 * run + slot;
+            uniform_ptr(reinterpret_cast<char*>(p.workspace) + kStreamKCounterBytes), (short)0,
+            s.sk_slots * kPartBytes, 0x00020000);
+        const int my_slot = sk_split > 0 ? run : 2 * run + slot;
         const int tr = t - dp_tiles;
         const int it_a = tr * nkb_total;
         const int w_lo = sk_owner(it_a), w_hi = sk_owner(it_a + nkb_total - 1);
@@ -892,7 +896,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
             v4f v[kG][kChunk];
 #pragma unroll
             for (int q = 0; q < kG; ++q) {
-              const int src = 2 * (w + q) + ((w + q) == w_lo ? lo_slot : 0);
+              const int src = sk_split > 0 ? w + q : 2 * (w + q) + ((w + q) == w_lo ? lo_slot : 0);
               const bool mine = kEarly && early && (w + q) == run;
 #pragma unroll
               for (int f = 0; f < kChunk; ++f)
@@ -1280,11 +1284,14 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
   // The same holds for their K parts.
   const int per_cu = (v == 4 || v == 7) ? 2 : 1;
   const int cap = std::min(num_cus * per_cu, kMaxStreamKGrid);
-  const int64_t slots = c.sk_split ? (int64_t)c.tiles * c.sk_split : cap;
+  const int64_t runs = c.sk_split ? (int64_t)c.tiles * c.sk_split : cap;
+  const int64_t slots = c.sk_split ? runs : 2 * runs;
   c.grid = !c.stream_k ? std::max(1, std::min(c.tiles, num_cus * per_cu))
-           : (int)std::min<int64_t>(cap, cdiv64(slots, 8) * 8);
-  if (c.stream_k && 2 * slots * c.bm * c.bn * 4 >= (1LL << 31)) {
-    c.stream_k = c.sk_split = 0;  // partial slots must stay 32-bit addressable
+           : (int)std::min<int64_t>(cap, cdiv64(runs, 8) * 8);
+  // Partial slots must stay 32-bit addressable, and every tile needs an
+  // arrival counter in the workspace's fixed counter region.
+  if (c.stream_k && (slots * c.bm * c.bn * 4 >= (1LL << 31) || c.tiles > kStreamKCounters)) {
+    c.stream_k = c.sk_split = 0;
     c.grid = std::max(1, std::min(c.tiles, num_cus));
   }
   c.sk_slots = c.stream_k ? (int)slots : 0;
@@ -1303,8 +1310,8 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
 size_t workspace_bytes_for(const GemmConfig& cfg, int layout, int m, int n, int groups) {
   (void)layout; (void)m; (void)n; (void)groups;
   if (!cfg.stream_k) return 0;
-  // Two fp32 partial tiles per run, then one arrival counter per tile.
-  return 2 * (size_t)cfg.sk_slots * cfg.bm * cfg.bn * sizeof(float) + (size_t)cfg.tiles * sizeof(int);
+  // The fixed counter region, then the fp32 partial tiles.
+  return kStreamKCounterBytes + (size_t)cfg.sk_slots * cfg.bm * cfg.bn * sizeof(float);
 }
 
 hipError_t launch_gemm(int layout, const GemmParams& p0, const GemmConfig& cfg,
@@ -1319,9 +1326,7 @@ hipError_t launch_gemm(int layout, const GemmParams& p0, const GemmConfig& cfg,
   s.sk_slots = cfg.sk_slots;
   s.group_m = cfg.group_m;
   s.k_rotate = cfg.k_rotate;
-  if (cfg.stream_k)
-    p.counters = reinterpret_cast<int*>(reinterpret_cast<char*>(p.workspace) +
-                                        2 * (size_t)cfg.sk_slots * cfg.bm * cfg.bn * sizeof(float));
+  if (cfg.stream_k) p.counters = reinterpret_cast<int*>(p.workspace);
   if (layout == kKGrouped) {
     switch (cfg.variant) {
       case 0: return launch_kgrouped<TileP256>(p, s, cfg.grid, stream);

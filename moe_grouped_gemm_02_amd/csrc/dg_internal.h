@@ -59,6 +59,15 @@ inline bool ue8m0_variant_built(int variant) {
   return variant == 0 || variant == 1 || variant == 4 || variant == 5 || variant == 6;
 }
 
+// Stream-K workspace layout.  Offset 0 holds a region of kStreamKCounters
+// int32 arrival counters (one per output tile); the fp32 partial-tile slots
+// follow it.  The counters sit at the same place whatever the configuration,
+// and every call leaves the counters it used at zero, so a workspace that was
+// zero-filled once serves later calls of any shape or configuration.
+// Configurations with more tiles than counters run without stream-K.
+constexpr int kStreamKCounters = 8192;
+constexpr size_t kStreamKCounterBytes = (size_t)kStreamKCounters * sizeof(int);
+
 // Tile configuration chosen on the host (deterministically, from the shape).
 struct GemmConfig {
   int variant;   // kernel instance (tile shape), index into the kernel table
@@ -66,7 +75,7 @@ struct GemmConfig {
   int bn;
   int stream_k;  // 1: K ranges of tiles divided among workgroups (stream-K)
   int sk_split;  // 0: equal runs of iterations; S >= 2: S equal parts per tile
-  int sk_slots;  // runs with partial-result slots (2 slots each)
+  int sk_slots;  // fp32 partial-tile slots: one per run with S parts per tile, two per equal run
   int grid;      // workgroups launched (persistent)
   int tiles;     // output tiles over all groups (masked: worst case)
   int group_m;   // raster group height in M tiles
@@ -80,7 +89,7 @@ struct Schedule {
   int n_tiles;
   int stream_k;
   int sk_split;
-  int sk_slots;
+  int sk_slots;      // see GemmConfig
   int group_m;
   int k_rotate;      // see GemmConfig
 };

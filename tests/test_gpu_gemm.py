@@ -188,3 +188,25 @@ def test_masked_all_empty_is_noop():
     a, sfa, b, sfb = _operands(None, 128, 128, seed=5, groups=2, a_shape=(2, 64, 128))
     out = run_masked(dg, a, sfa, b, sfb, [0, 0])
     assert np.all(out == SENTINEL)
+
+
+def test_workspace_reused_across_shapes_and_configurations():
+    # One workspace, zero-filled once and sized for the largest call, serves a
+    # sequence of stream-K GEMMs whose configurations differ (128x128 tiles in
+    # 4 parts, 64x64 tiles in 4 parts, the quantised-output form's widened
+    # tiles, then the first shape again).  The arrival counters sit at the
+    # same place for every configuration and each call leaves them at zero,
+    # so every output must match the oracle.
+    dg = require_gpu()
+    shapes = [(128, 7168, 16384), (128, 4096, 7168), (64, 2112, 7168), (128, 7168, 16384)]
+    size = max(dg.dg_get_workspace_size(m, n, k, 1) for m, n, k in shapes)
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    for i, (m, n, k) in enumerate(shapes):
+        a, sfa, b, sfb = _operands(m, n, k, seed=4100 + i)
+        full = torch.full((m, n), SENTINEL, dtype=torch.int16, device="cuda")
+        dg.dg_fp8_gemm_nt(dev(a), dev(sfa), dev(b), dev(sfb), full, workspace=ws)
+        rows = np.arange(0, m, 7)
+        ref = gemm.gemm_nt_ref(a[rows], sfa[:, rows], b, sfb)
+        check(bf16_to_f64(host(full)[rows]), ref, f"reused workspace, call {i}: {m}x{n}x{k}")
+    counters = host(ws[: 8192 * 4].view(torch.int32))
+    assert not np.any(counters), "arrival counters left non-zero"

@@ -147,6 +147,46 @@ def test_masked_equals_dense_on_valid_rows(mm):
             assert np.array_equal(d[g, :v], gemm.gemm_nt_ref(a[g, :v], sfa[g][:, :v], b[g], sfb[g]))
 
 
+def test_masked_group_and_row_indexing_pinned_by_closed_form():
+    # Independent of gemm_nt_ref: every value below is written out from the
+    # operands' construction.  Slice 0: A[g, r, 0] = 1.0 with activation
+    # scale (r % 5 + 1) f_g, f_g = 2^(g % 3); expert g's weights are (g + 1)
+    # at k = 0 with unit block scale.  Slice 1: A[g, r, 128] = 1.0 with unit
+    # scale; B[g][n, 128] = (n % 4 + 1) with block scale h_g = 0.5 (1 + g % 2).
+    # So on a valid row
+    #     D[g, r, n] = (g + 1)(r % 5 + 1) f_g + h_g (n % 4 + 1)     exactly,
+    # which pins the group of every row, the row within the group, the
+    # activation-scale group offset and the per-slice weight scale; rows at
+    # or past clamp(masked_m[g], 0, M_max) are not written ("DeepGEMM
+    # project introduction", Interfaces, Grouped GEMM (masked layout)).
+    m_max, n, k = 200, 136, 256
+    mm = np.array([-3, 0, 1, 129, m_max, m_max + 7])
+    groups = mm.size
+    one, codes = 0x38, [0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C]  # 1, 2, 3, 4, 5, 6
+    a = np.zeros((groups, m_max, k), dtype=np.uint8)
+    a[:, :, 0] = one
+    a[:, :, 128] = one
+    sfa = np.ones((groups, k // 128, m_max + 4), dtype=np.float32)  # ld > M_max
+    f = 2.0 ** (np.arange(groups) % 3)
+    h = 0.5 * (1 + np.arange(groups) % 2)
+    sfa[:, 0, :m_max] = (np.arange(m_max) % 5 + 1)[None, :] * f[:, None]
+    b = np.zeros((groups, n, k), dtype=np.uint8)
+    sfb = np.ones((groups, (n + 127) // 128, k // 128), dtype=np.float32)
+    for g in range(groups):
+        b[g, :, 0] = codes[g]
+        b[g, :, 128] = np.array(codes[:4], dtype=np.uint8)[np.arange(n) % 4]
+    sfb[:, :, 1] = h[:, None]
+    d, written = gemm.grouped_masked_ref(a, sfa, b, sfb, mm)
+    r = np.arange(m_max)[:, None]
+    c = np.arange(n)[None, :]
+    for g in range(groups):
+        valid = int(min(max(int(mm[g]), 0), m_max))
+        assert np.array_equal(written[g], np.arange(m_max) < valid)
+        expect = (g + 1.0) * (r % 5 + 1) * f[g] + h[g] * (c % 4 + 1)
+        assert np.array_equal(d[g, :valid], expect[:valid])
+        assert np.all(np.isnan(d[g, valid:]))
+
+
 def test_quantised_gemm_is_close_to_unquantised_product():
     # Gross sanity only (never a parity rule): the quantised product differs
     # from the bf16 product by a few percent, not by zero and not by O(1).
