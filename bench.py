@@ -7,10 +7,19 @@ every shape of the workload, quantise the bf16 activations per 1x128 tile
 points) on weights that were quantised per 128x128 block once, before timing
 (weights are converted offline, once per weight).
 
-The default workload is the dense decode sweep M = 128 over the six (N, K)
-pairs of DeepSeek-V3 shapes.  `--workload all` also measures every other
-workload shape (one line per shape on stderr, and a per-shape table in the
-JSON line).
+The default step is the largest workload: the MoE grouped GEMM in the
+contiguous layout, 4 experts x 8192 rows, N = 4096, K = 7168 (quantise the
+32768 x 7168 activations, then dg_grouped_contiguous).  Beside the step, the
+JSON line carries a per-shape record for every shape of the five workloads
+(dense M = 64; the M = 128 decode and M = 4096 prefill sweeps over six (N, K)
+pairs; contiguous; masked), each with both roofline fractions.
+
+Per-shape GEMM times: the primary figure is the median kernel duration from
+a rocprofv3 kernel trace (a child process: 10 warm-up launches, then 60
+timed ones per shape); the secondary is the mean over event-bracketed
+launches in this process.  `--workload decode128` times the decode sweep as
+the step instead; `--workload all` adds the pages' other table rows and the
+extra layouts to the per-shape records.
 
 Throughput accounting (the pages' own, which reproduces every row of the
 DeepGEMM performance tables, see tests/golden/):
@@ -82,8 +91,17 @@ def parse_args(argv=None):
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="decode128",
-                   help="decode128 (default) | all | a workload name from synth.workloads()")
+    p.add_argument("--workload", default="headline",
+                   help="headline (default: contiguous 4 x 8192 x 4096 x 7168) | decode128 | all | pages | "
+                        "a workload name from synth")
+    p.add_argument("--no-rocprof", action="store_true",
+                   help="skip the rocprofv3 kernel-trace pass (per-shape medians)")
+    p.add_argument("--per-shape", choices=("workloads", "step"), default="workloads",
+                   help="per-shape records for every shape of the five workloads (default) or the step's only")
+    p.add_argument("--trace-child", metavar="NAMES",
+                   help="internal: launch the GEMMs of these comma-separated workloads for a kernel trace")
+    p.add_argument("--trace-warmup", type=int, default=10)
+    p.add_argument("--trace-reps", type=int, default=60)
     p.add_argument("--scales", choices=("fp32", "ue8m0"), default="fp32",
                    help="scale format: fp32 (default) or power-of-two exponent bytes (UE8M0)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -106,10 +124,15 @@ def parse_args(argv=None):
 
 # --------------------------------------------------------------- workloads --
 
+HEADLINE = "contiguous_g4_m8192_n4096_k7168"
+
+
 def select_workloads(name):
     import synth
     wls = synth.workloads()
     extra = synth.pages_workloads() + synth.extra_workloads()
+    if name == "headline":
+        return [w for w in wls if w.name == HEADLINE]
     if name == "decode128":
         return [w for w in wls if w.layout == "dense" and w.m == 128]
     if name == "all":
@@ -118,7 +141,7 @@ def select_workloads(name):
         return [w for w in wls + extra if pages_key(w) is not None]
     pick = [w for w in wls + extra if w.name == name]
     if not pick:
-        raise SystemExit(f"unknown workload {name}; choose from decode128, all, pages, "
+        raise SystemExit(f"unknown workload {name}; choose from headline, decode128, all, pages, "
                          + ", ".join(w.name for w in wls + extra))
     return pick
 
@@ -360,12 +383,16 @@ def time_quant(dg, torch, p, reps=20):
 def cpu_baseline(wls, target_s, scales="fp32"):
     """The oracle, single-threaded, on a bounded sample of the workload.
 
-    Sample: for each shape, all M rows of A (at most 256) against the first
-    1024 columns of B (eight 128-row weight blocks).  The activations are
-    quantised inside the timed region, as in the GPU step; the weights are
-    quantised before it, as in the GPU step.  The shapes are visited in turn,
-    repeatedly, until about target_s seconds of oracle work are done.
-    Rate = sample flops / oracle seconds.
+    Sample, per shape: a 256-row slice of A (all rows when M <= 256; for the
+    grouped layouts the first 256 rows of expert 0) against the whole of
+    that expert's weight matrix when the step is a single large shape, or
+    against its first 1024 columns (eight 128-row weight blocks) when the
+    step is a sweep of shapes.  The activations are quantised inside the
+    timed region, as in the GPU step; the weights are quantised before it.
+    The sample is repeated until about target_s seconds of oracle work are
+    done.  Rate = sample flops / oracle seconds; the oracle's cost is linear
+    in the rows, so the whole step's oracle time is extrapolated from it and
+    labelled as such.
     """
     import synth
     from oracle import gemm, quant, ue8m0
@@ -382,13 +409,22 @@ def cpu_baseline(wls, target_s, scales="fp32"):
     else:
         quant_b, quant_a = quant.quant_128x128, quant.quant_1x128
 
+    whole_n = len(wls) == 1
     samples = []
+    step_flops = 0.0
     for wl in wls:
-        m = wl.m if wl.layout == "dense" else min(wl.m, 256)
-        ncols = min(wl.n, 1024)
+        m = min(wl.m, 256)
+        ncols = wl.n if whole_n else min(wl.n, 1024)
+        rows_all = wl.m * wl.groups if wl.layout == "contiguous" else (
+            int(synth.workload_masked_m(wl).sum()) if wl.layout == "masked" else wl.m)
+        step_flops += algorithmic_flops(rows_all, wl.n, wl.k)
+        # Expert 0's first rows and weights.  The generator fills tensors in
+        # row-major order from one stream, so drawing only the leading rows
+        # gives the same values as the full tensors' leading rows.
         xa = synth.bf16_normal((m, wl.k), wl.seed_a)
-        qb, sfb = quant_b(synth.bf16_normal((ncols, wl.k), wl.seed_b))
-        samples.append((wl, m, ncols, xa, qb, sfb))
+        xb = synth.bf16_normal((ncols, wl.k), wl.seed_b)
+        qb, sfb = quant_b(xb)
+        samples.append((wl, m, ncols, np.ascontiguousarray(xa), qb, sfb))
     flops = 0.0
     secs = 0.0
     runs = 0
@@ -401,17 +437,86 @@ def cpu_baseline(wls, target_s, scales="fp32"):
             secs += time.perf_counter() - t0
             flops += algorithmic_flops(m, ncols, wl.k)
             runs += 1
-    names = ", ".join(f"{wl.name}[:{m}, :{nc}]" for wl, m, nc, *_ in samples)
+    names = ", ".join(f"{wl.name}[rows :{m}, cols :{nc}]" for wl, m, nc, *_ in samples)
+    rate = flops / secs
     return {
-        "value": flops / secs / 1e12,
+        "value": rate / 1e12,
         "unit": "TFLOPS",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"single-threaded numpy oracle (quantise A per 1x128 + fp64 blockwise GEMM), {runs} runs "
-                  f"cycling over {names}; {secs:.1f} s of CPU work",
+        "sample": f"single-threaded numpy oracle (quantise A per 1x128 + fp64 blockwise GEMM) on a bounded slice: "
+                  f"{names}; {runs} runs, {secs:.1f} s of CPU work",
+        "extrapolated_step_s": round(step_flops / rate, 1),
+        "extrapolation": "whole step's oracle time = step flops / sample rate (cost is linear in rows and columns)",
         "cpu_model": _cpu_model(),
         "host_cores": os.cpu_count(),
     }
+
+
+# ------------------------------------------------------- rocprofv3 medians --
+
+def trace_child(dg, torch, names, warmup, reps, scales):
+    """Kernel-trace program: for each workload in turn, quantise once, then
+    launch its GEMM warmup + reps times (weights rotated), synchronising
+    between workloads.  Only GEMM launches are made after the set-up of each
+    workload, so the parent can split the traced gemm_kernel dispatches into
+    consecutive groups of warmup + reps."""
+    import synth
+    allw = {w.name: w for w in synth.workloads() + synth.pages_workloads() + synth.extra_workloads()}
+    for name in names:
+        p = Prepared(dg, torch, allw[name], scales)
+        p.quant(dg)
+        torch.cuda.synchronize()
+        for r in range(warmup + reps):
+            p.gemm(dg, r)
+        torch.cuda.synchronize()
+        print(json.dumps({"traced": name, "launches": warmup + reps}), flush=True)
+        del p
+        torch.cuda.empty_cache()
+
+
+def _under_rocprof():
+    return any("rocprof" in os.environ.get(v, "") for v in ("LD_PRELOAD", "HSA_TOOLS_LIB"))
+
+
+def rocprof_medians(names, scales, warmup=10, reps=60, timeout_s=600):
+    """Median kernel durations (us) per workload from a rocprofv3 kernel
+    trace of a child process (trace_child), or None where unavailable."""
+    import csv
+    import glob
+    import shutil
+    import tempfile
+    exe = shutil.which("rocprofv3")
+    if exe is None or _under_rocprof():
+        return None, "rocprofv3 not available" if exe is None else "already under rocprofv3"
+    out = tempfile.mkdtemp(prefix="dg_trace_", dir=os.environ.get("TMPDIR", "/tmp"))
+    cmd = [exe, "--kernel-trace", "--output-format", "csv", "-d", out, "-o", "kt", "--",
+           sys.executable, os.path.abspath(__file__), "--trace-child", ",".join(names),
+           "--trace-warmup", str(warmup), "--trace-reps", str(reps), "--scales", scales]
+    try:
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout_s, cwd=os.path.dirname(out))
+    except subprocess.TimeoutExpired:
+        shutil.rmtree(out, ignore_errors=True)
+        return None, f"rocprofv3 child timed out after {timeout_s} s"
+    done = [json.loads(x)["traced"] for x in r.stdout.splitlines() if x.startswith('{"traced"')]
+    files = glob.glob(os.path.join(out, "**", "*kernel_trace.csv"), recursive=True)
+    rows = []
+    for path in files:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if "gemm_kernel" in row["Kernel_Name"]:
+                    rows.append((int(row["Start_Timestamp"]), int(row["End_Timestamp"])))
+    shutil.rmtree(out, ignore_errors=True)
+    rows.sort()
+    per = warmup + reps
+    if done != list(names) or len(rows) != per * len(names):
+        return None, (f"rocprofv3 child incomplete (rc {r.returncode}, {len(done)}/{len(names)} workloads, "
+                      f"{len(rows)} gemm dispatches)")
+    med = {}
+    for i, name in enumerate(names):
+        durs = [(e - b) / 1e3 for b, e in rows[i * per + warmup:(i + 1) * per]]
+        med[name] = float(np.median(durs))
+    return med, f"rocprofv3 --kernel-trace: median of {reps} launches after {warmup} warm-up launches per shape"
 
 
 def _cpu_model():
@@ -610,14 +715,34 @@ def main(argv=None):
         print(json.dumps({"launches": args.reps, "workload": wl.name, "config": p.config}))
         return 0
 
+    if args.trace_child:
+        trace_child(dg, torch, args.trace_child.split(","), args.trace_warmup, args.trace_reps, args.scales)
+        return 0
+
+    import synth
     wls = select_workloads(args.workload)
-    headline = [w for w in wls if w.layout == "dense" and w.m == 128] or wls
+    headline = ([w for w in wls if w.layout == "dense" and w.m == 128] if args.workload == "decode128" else wls[:1])
+    # Per-shape records: every shape of the five workloads, plus (for
+    # --workload all / pages) the other shapes selected.
+    shape_wls = list(synth.workloads()) if args.per_shape == "workloads" else []
+    if args.workload in ("all", "pages"):
+        shape_wls += [w for w in wls if w not in shape_wls]
+    for w in headline:
+        if w not in shape_wls:
+            shape_wls.append(w)
+
+    # rocprofv3 kernel-trace medians (primary per-shape times), taken in a
+    # child process before this one touches the GPU.
+    medians, median_note = (None, "skipped (--no-rocprof)") if args.no_rocprof else rocprof_medians(
+        [w.name for w in shape_wls], args.scales)
+    if medians is None:
+        print(f"note: no rocprofv3 medians: {median_note}", file=sys.stderr)
+
     preps = [Prepared(dg, torch, w, args.scales) for w in headline]
     torch.cuda.synchronize()
-
-    # Per-shape pass (not the benchmark value): every GEMM launch bracketed by
-    # events, which also picks the dominant kernel - the GEMM configuration
-    # with the most total time.
+    # Per-launch pass (not the benchmark value): every GEMM launch bracketed
+    # by events, which also picks the dominant kernel - the GEMM
+    # configuration with the most total time.
     _, shape_ms = time_steps(dg, torch, preps, args.steps, args.warmup)
     by_kernel = {}
     for i, p in enumerate(preps):
@@ -627,29 +752,13 @@ def main(argv=None):
 
     # The timed pass: W warmup steps, then exactly K steps between two torch
     # events; only the dominant kernel's launches carry HIP events (each
-    # event record costs the stream ~0.8 us, ~19 us per step if every launch
-    # were bracketed).
+    # event record costs the stream ~0.8 us).
     total_ms, gemm_ms = time_steps(dg, torch, preps, args.steps, args.warmup, instrument=idx)
     ms_per_step = total_ms / args.steps
     step_flops = sum(p.flops for p in preps)
     value = step_flops / (ms_per_step * 1e-3) / 1e12
-
-    per_shape = []
-    for i, p in enumerate(preps):
-        t = float(np.mean(shape_ms[:, i])) * 1e-3
-        per_shape.append(shape_record(p, t, time_quant(dg, torch, p)))
-
-    extra = []
-    if args.workload in ("all", "pages"):
-        for w in wls:
-            if w in headline:
-                continue
-            p = Prepared(dg, torch, w, args.scales)
-            _, g_ms = time_steps(dg, torch, [p], max(5, args.steps // 2), 2)
-            extra.append(shape_record(p, float(np.mean(g_ms[:, 0])) * 1e-3, time_quant(dg, torch, p)))
-            print(json.dumps(extra[-1]), file=sys.stderr, flush=True)
-            del p
-            torch.cuda.empty_cache()
+    head_quant_ms = [time_quant(dg, torch, p) for p in preps]
+    head_shape_ms = {p.wl.name: float(np.mean(shape_ms[:, i])) for i, p in enumerate(preps)}
 
     # Roofline of the dominant kernel, from its launches in the timed pass.
     # HBM-bound below the ridge point (peak flops / peak bytes), MFMA-bound
@@ -668,6 +777,9 @@ def main(argv=None):
     # cycles x SIMDs, at the clock the GPU actually ran), same condition.
     busy = [read_mfma_busy(preps[i].wl.name, args.scales) for i in idx]
     mfma_busy = float(np.mean(busy)) if busy and all(x is not None for x in busy) else None
+    med_us = None
+    if medians is not None:
+        med_us = float(np.mean([medians[preps[i].wl.name] for i in idx]))
     roofline = {
         "bound": "mfma" if mfma_bound else "hbm",
         "achieved": round(achieved, 1),
@@ -684,13 +796,40 @@ def main(argv=None):
         "mean_algorithmic_bytes_per_launch": mean_bytes,
         "mean_algorithmic_flops_per_launch": mean_flops,
         "mean_launch_us": round(mean_dur * 1e6, 3),
+        "rocprof_median_us": round(med_us, 3) if med_us is not None else None,
+        "frac_from_rocprof_median": (round((mean_flops / (med_us * 1e-6) / 1e12 if mfma_bound
+                                            else mean_bytes / (med_us * 1e-6) / 1e9) / peak, 4)
+                                     if med_us is not None else None),
     }
-
+    copies = [len(p.b) for p in preps]
+    step_bytes = sum(p.bytes for p in preps)
     vs = None
-    if headline and all(pages_key(w) is not None for w in headline):
+    if all(pages_key(p.wl) is not None for p in preps):
         page_t = sum(p.flops / (PAGES_TFLOPS[pages_key(p.wl)] * 1e12) for p in preps)
         vs = round(value / (step_flops / page_t / 1e12), 4)
+    del preps
+    torch.cuda.empty_cache()
 
+    # Per-shape records, one workload at a time (event-timed here; the
+    # rocprofv3 median is the primary time where present).
+    per_shape = []
+    for w in shape_wls:
+        if w.name in head_shape_ms:
+            i = [h.name for h in headline].index(w.name)
+            p = Prepared(dg, torch, w, args.scales)
+            ev_ms, q_ms = head_shape_ms[w.name], head_quant_ms[i]
+        else:
+            p = Prepared(dg, torch, w, args.scales)
+            _, g_ms = time_steps(dg, torch, [p], max(5, args.steps // 2), 2)
+            ev_ms, q_ms = float(np.mean(g_ms[:, 0])), time_quant(dg, torch, p)
+        med = medians.get(w.name) if medians else None
+        per_shape.append(shape_record(p, ev_ms * 1e-3, q_ms, med))
+        if args.workload in ("all", "pages"):
+            print(json.dumps(per_shape[-1]), file=sys.stderr, flush=True)
+        del p
+        torch.cuda.empty_cache()
+
+    head = headline[0]
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -702,20 +841,28 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": vs,
+        "vs_baseline_note": ("value / the pages' H800 GEMM-only TFLOPS for the same shapes (context on other "
+                             "hardware, not the target; the step here also quantises the activations)"
+                             if vs is not None else None),
         "dtype": "fp8_e4m3",
         "data": "synthetic",
         "config": {
-            "workload": "dense_decode_sweep_m128" if len(headline) > 1 else headline[0].name,
-            "m": headline[0].m,
+            "workload": "dense_decode_sweep_m128" if len(headline) > 1 else head.name,
+            "layout": head.layout,
+            "groups": head.groups,
+            "m_per_group": head.m,
             "nk_pairs": [[w.n, w.k] for w in headline],
-            "step": "dg_quant_1x128(A) + GEMM per shape; weights quantised once before timing",
+            "step": "dg_quant_1x128(A) + GEMM; weights quantised once before timing",
             "scales": args.scales,
-            "weight_rotation_copies": [len(p.b) for p in preps],
+            "weight_rotation_copies": copies,
             "num_cus": dg.dg_get_num_cus(),
         },
-        "step_gbps": round(sum(p.bytes for p in preps) / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "roofline": roofline,
-        "per_shape": per_shape + extra,
+        "per_shape_timing": {"primary": median_note if medians else None,
+                             "secondary": "mean over event-bracketed launches in this process "
+                                          "(includes ~1 us of dispatch per launch)"},
+        "per_shape": per_shape,
     }
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(headline, args.cpu_seconds, args.scales)
@@ -723,7 +870,10 @@ def main(argv=None):
     return 0
 
 
-def shape_record(p, t, quant_ms):
+def shape_record(p, t_events, quant_ms, median_us=None):
+    """One shape's figures.  Time: the rocprofv3 median when given, else the
+    event-timed mean (both are recorded)."""
+    t = median_us * 1e-6 if median_us is not None else t_events
     tflops = p.flops / t / 1e12
     gbps = p.bytes / t / 1e9
     key = pages_key(p.wl)
@@ -737,6 +887,9 @@ def shape_record(p, t, quant_ms):
         "n": p.wl.n,
         "k": p.wl.k,
         "gemm_us": round(t * 1e6, 3),
+        "gemm_us_source": "rocprofv3 median" if median_us is not None else "events mean",
+        "gemm_us_rocprof_median": round(median_us, 3) if median_us is not None else None,
+        "gemm_us_events_mean": round(t_events * 1e6, 3),
         "tflops": round(tflops, 2),
         "gbps": round(gbps, 1),
         "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),

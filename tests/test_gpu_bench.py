@@ -22,7 +22,8 @@ def _run(args, timeout=240):
 
 @pytest.mark.gpu
 def test_json_line_contract():
-    r = _run(["--workload", "dense_m64_n2112_k7168", "--steps", "3", "--warmup", "1", "--cpu-seconds", "1"])
+    r = _run(["--workload", "dense_m64_n2112_k7168", "--steps", "3", "--warmup", "1", "--cpu-seconds", "1",
+              "--per-shape", "step"])
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [line for line in r.stdout.splitlines() if line.strip()]
     assert len(lines) == 1, "exactly one line on stdout"
@@ -35,6 +36,9 @@ def test_json_line_contract():
     assert ROOFLINE_KEYS <= set(roof)
     assert roof["bound"] in ("hbm", "mfma") and 0 < roof["frac"] < 1
     assert abs(roof["achieved"] / roof["peak"] - roof["frac"]) < 1e-3
+    shape = out["per_shape"][0]
+    assert len(out["per_shape"]) == 1 and shape["workload"] == "dense_m64_n2112_k7168"
+    assert shape["gemm_us_rocprof_median"] is None or shape["gemm_us_source"] == "rocprofv3 median"
     cpu = out["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1
 
