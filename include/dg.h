@@ -86,6 +86,26 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
                    int64_t ld_sfa, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * dg_fp8_gemm_nt without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Operands, output, rules and errors are
+ * those of dg_fp8_gemm_nt.  The split-K partials and arrival counters live
+ * in a scratch array inside the library, one per GPU, of 32 MiB + 32 KiB,
+ * held until the process ends; a shape whose configuration needs more
+ * (dg_get_workspace_size(m, n, k, 1) > 33587200, e.g. a 4096 x 2112 x 7168
+ * GEMM, which divides the K ranges of 256 x 256 tiles) is rejected with
+ * DG_ERR_WORKSPACE before anything is enqueued.  Nothing is allocated: the
+ * first call on a GPU looks up that GPU's array and enqueues one small kernel
+ * on `stream` that clears its counters; every call leaves them at zero.
+ * All calls on one GPU share its array, so calls that may run at the same
+ * time on one GPU (on different streams, or graphs launched concurrently)
+ * race and must be serialised by the caller.
+ */
+int dg_fp8_gemm_nt_noalloc(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                           uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
+                           int64_t ld_sfa, void* stream);
+
+/*
  * Grouped GEMM, contiguous layout (m_grouped_gemm_fp8_fp8_bf16_nt_contiguous;
  * project introduction, section "Grouped GEMM (contiguous layout)"): the
  * tokens of all experts are concatenated along M; only M is grouped, N and K

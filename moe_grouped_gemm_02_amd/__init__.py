@@ -32,6 +32,7 @@ _S = ctypes.c_size_t
 
 _SIGNATURES = {
     "dg_fp8_gemm_nt": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _L, _L, _P, _S, _P]),
+    "dg_fp8_gemm_nt_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _L, _L, _P]),
     "dg_grouped_contiguous": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _L, _P, _S, _P]),
     "dg_grouped_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _L, _P, _S, _P]),
     "dg_fp8_gemm_nt_ue8m0": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _L, _L, _L, _L, _P, _S, _P]),
@@ -209,6 +210,26 @@ def _masked(fn, a, sfa, b, sfb, d, masked_m, expected_m, workspace, ue8m0):
 def dg_fp8_gemm_nt(a, sfa, b, sfb, d, workspace=None):
     """d[m][n] = bf16(A . B^T) with 1x128 (sfa [K/128][ld]) and 128x128 scales."""
     return _gemm_nt("dg_fp8_gemm_nt", a, sfa, b, sfb, d, workspace, False)
+
+
+def dg_fp8_gemm_nt_noalloc(a, sfa, b, sfb, d):
+    """dg_fp8_gemm_nt with the library's own per-GPU scratch instead of a
+    workspace (allocates nothing; calls on one GPU must not overlap)."""
+    _expect(a, "a", _U8, 2), _expect(b, "b", _U8, 2), _expect(d, "d", _BF, 2)
+    _expect(sfa, "sfa", _sf_dtype(False), 2), _expect(sfb, "sfb", _sf_dtype(False), 2)
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k or tuple(d.shape) != (m, n):
+        raise ValueError("shape mismatch between a, b and d")
+    if sfa.shape[0] != k // 128 or tuple(sfb.shape) != _sfb_shape(n, k, False):
+        raise ValueError(f"scale shapes must be sfa [K/128][ld] and sfb {_sfb_shape(n, k, False)}")
+    for t, nm in ((a, "a"), (b, "b"), (d, "d"), (sfa, "sfa")):
+        _row_major(t, nm)
+    _contig(sfb, "sfb")
+    _check("dg_fp8_gemm_nt_noalloc", _lib.dg_fp8_gemm_nt_noalloc(
+        _ptr(a), _ptr(sfa), _ptr(b), _ptr(sfb), _ptr(d), m, n, k, a.stride(0), b.stride(0),
+        d.stride(0), sfa.stride(0), _stream(d)))
+    return d
 
 
 def dg_fp8_gemm_nt_ue8m0(a, sfa, b, sfb, d, workspace=None):

@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "dg.h"
 #include "dg_internal.h"
@@ -351,9 +352,75 @@ int quant_128x128_impl(const uint16_t* w, uint8_t* q, void* sf, int rows, int co
   return ok();
 }
 
+// ------------------------------------------------- no-allocation dense GEMM --
+// Device scratch of dg_fp8_gemm_nt_noalloc, for callers that cannot allocate:
+// the stream-K arrival counters (the first kStreamKCounterBytes) and fp32
+// partial tiles of one call.  The array lives in the loaded code object, one
+// copy per GPU, until the process ends.  Host code never uses the array's
+// name as an address: each device's copy is looked up once with
+// hipGetSymbolAddress and kept in g_scratch.
+constexpr size_t kNoAllocScratchBytes = dg::kStreamKCounterBytes + ((size_t)32 << 20);
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+__global__ void clear_words(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// This device's scratch address; on the first call for a device, also
+// enqueues (on `stream`) a kernel that clears the counter region.  Every
+// GEMM call leaves the counters it used at zero, so later calls need no
+// clearing.  Returns DG_SUCCESS or an error status.
+int noalloc_scratch(void* stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(DG_ERR_HIP, "cannot query the current device");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DG_ERR_HIP, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return fail(DG_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    const int words = (int)(dg::kStreamKCounterBytes / 4);
+    hipLaunchKernelGGL(clear_words, dim3(words / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<uint32_t*>(ptr), words);
+    const hipError_t le = hipGetLastError();
+    if (le != hipSuccess) return fail(DG_ERR_HIP, "scratch clear launch failed: %s", hipGetErrorString(le));
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return DG_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
+
+int dg_fp8_gemm_nt_noalloc(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
+                           uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
+                           int64_t ld_sfa, void* stream) {
+  int st = check_gemm_common(a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa);
+  if (st != DG_SUCCESS) return st;
+  if (m == 0 || n == 0) return ok();
+  if (!dg::plannable(dg::kDense, m, n, 1))
+    return fail(DG_ERR_UNSUPPORTED_SHAPE, "too many output tiles (m=%d n=%d)", m, n);
+  const int cus = resolve_num_cus();
+  if (cus < 0) return fail(DG_ERR_HIP, "cannot query the device's compute-unit count");
+  const dg::GemmConfig cfg = dg::choose_config(dg::kDense, m, n, k, 1, cus);
+  const size_t need = dg::workspace_bytes_for(cfg, dg::kDense, m, n, 1);
+  if (need > kNoAllocScratchBytes)
+    return fail(DG_ERR_WORKSPACE, "m=%d n=%d k=%d needs %zu bytes of scratch; the no-allocation GEMM holds %zu",
+                m, n, k, need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    st = noalloc_scratch(stream, &ws);
+    if (st != DG_SUCCESS) return st;
+  }
+  return gemm_nt_impl(a, sfa, b, sfb, d, m, n, k, lda, ldb, ldd, ld_sfa, ws, need > 0 ? kNoAllocScratchBytes : 0,
+                      stream, false);
+}
 
 int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const float* sfb,
                    uint16_t* d, int m, int n, int k, int64_t lda, int64_t ldb, int64_t ldd,
