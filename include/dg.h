@@ -92,7 +92,7 @@ int dg_fp8_gemm_nt(const uint8_t* a, const float* sfa, const uint8_t* b, const f
  * those of dg_fp8_gemm_nt.  The split-K partials and arrival counters live
  * in a scratch array inside the library, one per GPU, of 32 MiB + 32 KiB,
  * held until the process ends; a shape whose configuration needs more
- * (dg_get_workspace_size(m, n, k, 1) > 33587200, e.g. a 4096 x 2112 x 7168
+ * (dg_get_workspace_size(m, n, k, 1) > 33587200, e.g. a 4096 x 2816 x 7168
  * GEMM, which divides the K ranges of 256 x 256 tiles) is rejected with
  * DG_ERR_WORKSPACE before anything is enqueued.  Nothing is allocated: the
  * first call on a GPU looks up that GPU's array and enqueues one small kernel

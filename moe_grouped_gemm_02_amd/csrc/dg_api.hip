@@ -119,7 +119,8 @@ int run_gemm(int layout, dg::GemmParams& p, int rows, int groups, void* ws, size
   const int cus = resolve_num_cus();
   if (cus < 0) return fail(DG_ERR_HIP, "cannot query the device's compute-unit count");
   const bool qout = p.dq != nullptr;
-  const dg::GemmConfig cfg = dg::choose_config(layout, rows, p.n, p.k, groups, cus, expected_m, qout);
+  const bool narrow_ok = !p.sf_ue8m0 && !p.majors && layout != dg::kKGrouped;
+  const dg::GemmConfig cfg = dg::choose_config(layout, rows, p.n, p.k, groups, cus, expected_m, qout, narrow_ok);
   if (layout == dg::kKGrouped && !dg::kgrouped_variant_built(cfg.variant))
     return fail(DG_ERR_UNSUPPORTED_SHAPE, "tile variant %d is not built for the K-grouped layout", cfg.variant);
   if (p.majors && !dg::majors_variant_built(cfg.variant))
@@ -619,14 +620,15 @@ size_t dg_get_workspace_size(int m, int n, int k, int num_groups) {
   // select.
   size_t worst = 0;
   const int hints[] = {0, 1, 64, 65, 128, 129, 256, 257};
-  for (int qout = 0; qout <= 1; ++qout)
-    for (int layout = dg::kDense; layout <= dg::kMasked; ++layout)
-      for (int h : hints) {
-        if ((h && layout != dg::kMasked) || !dg::plannable(layout, m, n, num_groups)) break;
-        const dg::GemmConfig c = dg::choose_config(layout, m, n, k, num_groups, cus, h, qout != 0);
-        const size_t need = dg::workspace_bytes_for(c, layout, m, n, num_groups);
-        if (need > worst) worst = need;
-      }
+  for (int narrow = 0; narrow <= 1; ++narrow)
+    for (int qout = 0; qout <= 1; ++qout)
+      for (int layout = dg::kDense; layout <= dg::kMasked; ++layout)
+        for (int h : hints) {
+          if ((h && layout != dg::kMasked) || !dg::plannable(layout, m, n, num_groups)) break;
+          const dg::GemmConfig c = dg::choose_config(layout, m, n, k, num_groups, cus, h, qout != 0, narrow != 0);
+          const size_t need = dg::workspace_bytes_for(c, layout, m, n, num_groups);
+          if (need > worst) worst = need;
+        }
   return worst;
 }
 

@@ -95,6 +95,22 @@ __device__ __forceinline__ void wait_vm() {
 
 __device__ __forceinline__ void barrier_all() { asm volatile("s_barrier" : : : "memory"); }
 
+// Wait until at most NEWER stages of this wave's DMAs are in flight (the
+// stages issued after the one the loop needs next).  Waves issue different
+// numbers of DMAs per stage (T::dmas_of_wave), so the count is picked per
+// run of waves with equal counts.
+template <class T, int NEWER, int W = 0>
+__device__ __forceinline__ void wait_stage(int wave) {
+  if constexpr (W + 1 >= T::kWaves) {
+    wait_vm<NEWER * T::dmas_of_wave(W)>();
+  } else if constexpr (T::dmas_of_wave(W + 1) == T::dmas_of_wave(W)) {
+    wait_stage<T, NEWER, W + 1>(wave);
+  } else {
+    if (wave <= W) wait_vm<NEWER * T::dmas_of_wave(W)>();
+    else wait_stage<T, NEWER, W + 1>(wave);
+  }
+}
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
@@ -211,7 +227,11 @@ __device__ __forceinline__ v4f mfma_fp8_slice(const v8i& a, const v8i& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
+// SB_BYTES: LDS bytes a stage keeps for the slice's weight scales: 1 KB (one
+// 16-byte DMA per lane: the K-grouped layout's per-column scales of B), or
+// 256 bytes (one 4-byte DMA per lane: up to 64 weight-scale blocks), which
+// lets a third stage of the 256 x 160 tile fit in the 160 KB of LDS.
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, int SB_BYTES = 1024>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
   static constexpr int kWaves = WM * WN;
@@ -223,9 +243,13 @@ struct Tile {
   // in the same region (A rows, B rows, scales) - a compile-time choice.
   static constexpr int kAInstr = BM / 8;            // 1 KB DMA instructions per slice
   static constexpr int kBInstr = BN / 8;
-  static constexpr int kAJ = kAInstr / kWaves;      // per-wave instruction counts
-  static constexpr int kBJ = kBInstr / kWaves;
-  static constexpr int kLPW = kAJ + kBJ;            // A/B DMAs per wave per stage; waves 0
+  // Per-wave instruction rounds: wave w issues A instructions j * kWaves + w
+  // for j < kAJ while that index is below kAInstr (the last round may be
+  // partial when the tile's rows do not split evenly over the waves), then
+  // the B instructions the same way.
+  static constexpr int kAJ = (kAInstr + kWaves - 1) / kWaves;
+  static constexpr int kBJ = (kBInstr + kWaves - 1) / kWaves;
+  static constexpr int kLPW = kAJ + kBJ;            // A/B DMA rounds per wave per stage; waves 0
                                                     // and 1 issue one more each, for the
                                                     // activation and the weight scales
   static constexpr int kIssue = kLPW + 1;           // DMA pieces per wave per stage
@@ -239,7 +263,14 @@ struct Tile {
   static constexpr int kSpreadRows = kWaves < 8 ? 0 : ((BM * BN >= 256 * 256) ? 1 : FM);
   static constexpr int kSOffInstr = kAInstr + kBInstr;
   static constexpr int kSBOff = (kAInstr + kBInstr + 1) * 1024;  // weight scales of the slice
-  static constexpr int kStageBytes = (kAInstr + kBInstr + 2) * 1024;
+  static constexpr int kSBBytes = SB_BYTES;
+  static constexpr int kStageBytes = (kAInstr + kBInstr + 1) * 1024 + SB_BYTES;
+  // DMA instructions wave w issues per stage: its A and B instructions plus,
+  // for waves 0 and 1, the scale DMA.
+  static constexpr int dmas_of_wave(int w) {
+    return (kAInstr / kWaves + (w < kAInstr % kWaves ? 1 : 0)) + (kBInstr / kWaves + (w < kBInstr % kWaves ? 1 : 0)) +
+           (w < 2 ? 1 : 0);
+  }
   static constexpr int kBOff = BM * 128;
   static constexpr int kSOff = (BM + BN) * 128;
   static constexpr bool kOneSB = (128 % TN) == 0;   // wave columns inside one 128-block
@@ -248,11 +279,11 @@ struct Tile {
   // provides the overlap instead).
   static constexpr bool kPipe = kWaves <= 4;
   static_assert(TM % 16 == 0 && TN % 16 == 0, "bad tile");
-  static_assert(kAInstr % kWaves == 0 && kBInstr % kWaves == 0, "tile rows must split evenly over waves");
+  static_assert(SB_BYTES == 1024 || SB_BYTES == 256, "weight-scale slot of 1 KB or 256 bytes");
   static_assert(BM <= 256, "one scale instruction covers 256 rows");
   static_assert(STAGES >= 2, "need two stages");
   static_assert(kWaves >= 2, "waves 0 and 1 load the scales");
-  static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS overflow");
+  static_assert(STAGES * kStageBytes + 16 <= 160 * 1024, "LDS overflow");
 };
 
 // Decode a linear work-unit index into a tile.  XCD-aware: workgroup w runs on
@@ -515,6 +546,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
         const uint32_t stage_lds = smem_base + buf * T::kStageBytes;
         if constexpr (j < T::kAJ) {
           const int instr = j * T::kWaves + wave;
+          if (T::kAInstr % T::kWaves != 0 && instr >= T::kAInstr) return;  // partial last round
           const int q = instr * 64 + lane;
           if constexpr (kAT) {
             // K row kr of the slice, chunk position cp; the chunk holds rows
@@ -535,7 +567,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
           }
         } else if constexpr (j < T::kLPW) {
           constexpr int jb = j - T::kAJ;
-          const int instr = (T::kAJ + jb) * T::kWaves + wave;
+          if (T::kBInstr % T::kWaves != 0 && jb * T::kWaves + wave >= T::kBInstr) return;  // partial last round
+          const int instr = T::kAInstr + jb * T::kWaves + wave;
           const int q = (jb * T::kWaves + wave) * 64 + lane;
           if constexpr (kBT) {
             constexpr int C = T::BN / 16;
@@ -566,10 +599,15 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
               // Activation scales of the slice: rows m0 .. m0 + 4*63 + 3.
               const int r4 = min(m0 + 4 * lane, (int)p.ld_sfa - 4);
               dma16(stage_lds + T::kSOffInstr * 1024, SA, (uint32_t)(kb * p.ld_sfa + r4) * 4u);
-            } else if (SF == kScaleRowB && wave == 1) {
+            } else if (SF == kScaleRowB) {
               // Row scales of B: columns n0 .. n0 + 4*63 + 3 of the slice.
-              const int c4 = min(n0 + 4 * lane, (int)p.ld_sfb - 4);
-              dma16(stage_lds + T::kSBOff, SB, (uint32_t)(kb * p.ld_sfb + c4) * 4u);
+              if constexpr (SF == kScaleRowB) {
+                static_assert(T::kSBBytes == 1024, "per-column B scales need a 1 KB slot");
+                if (wave == 1) {
+                  const int c4 = min(n0 + 4 * lane, (int)p.ld_sfb - 4);
+                  dma16(stage_lds + T::kSBOff, SB, (uint32_t)(kb * p.ld_sfb + c4) * 4u);
+                }
+              }
             } else if (wave == 1) {
               // Weight scales of the slice for the tile's column blocks (lane l:
               // block cb_first + l; lanes past the last block repeat it).
@@ -636,8 +674,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
         if (nkb > 0) issue_stage(kb_at(0), 0);
         if (nkb > 1) {
           issue_stage(kb_at(1), 1);
-          if (wave < 2) wait_vm<T::kLPW + 1>();
-          else wait_vm<T::kLPW>();
+          wait_stage<T, 1>(wave);
         } else {
           wait_vm<0>();
         }
@@ -714,8 +751,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
           // Wait for this wave's DMAs of stage `it` (newer stages may stay in
           // flight), then barrier so every wave's part of the stage has landed.
           if (it + T::STAGES - 2 < nkb) {
-            if (wave < 2) wait_vm<(T::STAGES - 2) * (T::kLPW + 1)>();
-            else wait_vm<(T::STAGES - 2) * T::kLPW>();
+            wait_stage<T, T::STAGES - 2>(wave);
           } else {
             wait_vm<0>();
           }
@@ -913,7 +949,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
         // chunks of fragments with up to kG runs' loads in flight; on the
         // early path this workgroup's own run comes from registers.
         const int lo_slot = sk_start(w_lo) < it_a ? 1 : 0;  // run w_lo began in an earlier tile
-        constexpr int kChunk = kFrag < 8 ? kFrag : 8;
+        // Fragments per chunk: the largest divisor of kFrag up to 8.
+        constexpr int kChunk = kFrag % 8 == 0 ? 8 : kFrag % 5 == 0 ? 5 : kFrag % 4 == 0 ? 4 : kFrag % 3 == 0 ? 3 : kFrag % 2 == 0 ? 2 : 1;
         constexpr int kG = T::kWaves >= 16 ? 1 : (kFrag >= 32 ? 2 : 4);
         static_assert(kFrag % kChunk == 0, "fragments must split into whole chunks");
         static_for<kFrag / kChunk>([&](auto cc) {
@@ -1103,6 +1140,12 @@ using TileS64w8 = Tile<64, 64, 2, 4, 4>;     // decode small tiles: 8 waves, 32x
 using TileW128w16 = Tile<128, 256, 4, 4, 3>; // decode wide N: 16 waves, 32x64 per wave
 using TileV128 = Tile<128, 256, 1, 4, 3>;    // decode: every wave holds all 128 rows, 128x64 per wave
 using TileV128w8 = Tile<128, 256, 1, 8, 3>;  // the same with 8 waves, 128x32 per wave
+// Non-power-of-two BLOCK_N (DeepGEMM project introduction, Optimisations,
+// unaligned block sizes): 256 x 160, 8 waves of 64 x 80, three stages (the
+// 256-byte weight-scale slot makes 3 x 54528 bytes fit the 160 KB of LDS).
+// 4096 x 2112 gives 224 such tiles, one wave on 256 CUs, against 144 of
+// 256 x 256.
+using TileP160 = Tile<256, 160, 4, 2, 3, 256>;
 
 struct Variant {
   int bm, bn, threads;
@@ -1119,6 +1162,7 @@ constexpr Variant kVariants[] = {
     {TileW128w16::BM, TileW128w16::BN, TileW128w16::kThreads},
     {TileV128::BM, TileV128::BN, TileV128::kThreads},
     {TileV128w8::BM, TileV128w8::BN, TileV128w8::kThreads},
+    {TileP160::BM, TileP160::BN, TileP160::kThreads},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -1228,7 +1272,8 @@ bool variant_quantises_output(int variant) {
   return variant >= 0 && variant < kNumVariants && kVariants[variant].bn % 128 == 0;
 }
 
-GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cus, int expected_m, bool qout) {
+GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cus, int expected_m, bool qout,
+                         bool narrow_ok) {
   // m: dense M, contiguous M_total, masked M_max.  The rules below come from
   // sweeps over tile variants on the benchmark shapes.  For the masked
   // layout a host hint of the typical valid rows per group replaces M_max in
@@ -1249,6 +1294,13 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
     v = (rows > 64 && (10 * t128 >= 7 * num_cus || nkb >= 64)) ? 6 : 4;
   } else if (tiles_of(256, 256) >= num_cus / 2) {
     v = 0;
+    // Non-power-of-two BLOCK_N: when 256 x 256 tiles fill under 70% of the
+    // CUs but one round of 256 x 160 tiles fills at least 80% of them, the
+    // narrower tile runs data-parallel in one wave (measured 4096 x 2112 x
+    // 7168: 103.4 us against 113.6 us for 256 x 256 tiles in equal
+    // stream-K runs).
+    const int64_t t256 = tiles_of(256, 256), t160 = tiles_of(256, 160);
+    if (narrow_ok && !qout && layout != kKGrouped && 10 * t256 < 7 * (int64_t)num_cus && 5 * t160 >= 4 * (int64_t)num_cus && t160 <= num_cus) v = 11;
   } else {
     // Mid-size M (e.g. 1024 rows in all): 128-row tiles, 256 columns wide
     // unless 128 columns fill the CUs' last round better (measured on the
@@ -1395,7 +1447,8 @@ hipError_t launch_gemm(int layout, const GemmParams& p0, const GemmConfig& cfg,
     case 7: return launch_layout<TileS64w8, kScaleF32>(layout, p, s, cfg.grid, stream);
     case 8: return launch_layout<TileW128w16, kScaleF32>(layout, p, s, cfg.grid, stream);
     case 9: return launch_layout<TileV128, kScaleF32>(layout, p, s, cfg.grid, stream);
-    default: return launch_layout<TileV128w8, kScaleF32>(layout, p, s, cfg.grid, stream);
+    case 10: return launch_layout<TileV128w8, kScaleF32>(layout, p, s, cfg.grid, stream);
+    default: return launch_layout<TileP160, kScaleF32>(layout, p, s, cfg.grid, stream);
   }
 }
 

@@ -102,8 +102,10 @@ bool plannable(int layout, int m, int n, int groups);
 // used to pick the tile shape.
 // qout: the call also quantises its output, which needs tiles whose columns
 // are whole 128-column blocks.
+// narrow_ok: the 256 x 160 tile (built for fp32 scales with both operands
+// K-major, dense / contiguous / masked) may be chosen.
 GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cus, int expected_m = 0,
-                         bool qout = false);
+                         bool qout = false, bool narrow_ok = true);
 // Whether a tile variant's columns are whole 128-column blocks.
 bool variant_quantises_output(int variant);
 size_t workspace_bytes_for(const GemmConfig& cfg, int layout, int m, int n, int groups);

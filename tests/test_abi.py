@@ -124,9 +124,13 @@ def test_stream_k_workspace_size():
     # Large tiles that fill under 70% of the CUs, long K: equal runs over all
     # CUs, two partial slots per run (a run may end in one tile and begin the
     # next).
-    fields = dict(kv.split("=") for kv in dg.dg_describe_config(dg.LAYOUT_DENSE, 4096, 2112, 7168, 1, 256).split())
+    fields = dict(kv.split("=") for kv in dg.dg_describe_config(dg.LAYOUT_DENSE, 4096, 2816, 7168, 1, 256).split())
     assert int(fields["stream_k"]) == 1 and int(fields["sk_split"]) == 0 and int(fields["grid"]) == 256
     assert int(fields["workspace"]) == counters + 2 * 256 * 256 * 256 * 4
+    # Non-power-of-two BLOCK_N: 4096 x 2112 fills 144 of 256 CUs with 256 x 256
+    # tiles but 224 with 256 x 160 ones, which then run data-parallel.
+    fields = dict(kv.split("=") for kv in dg.dg_describe_config(dg.LAYOUT_DENSE, 4096, 2112, 7168, 1, 256).split())
+    assert (fields["bm"], fields["bn"], fields["stream_k"], fields["tiles"]) == ("256", "160", "0", "224")
     dense_full = dict(kv.split("=") for kv in dg.dg_describe_config(dg.LAYOUT_DENSE, 4096, 4096, 7168, 1, 256).split())
     assert int(dense_full["tiles"]) == 256 and int(dense_full["stream_k"]) == 0 and int(dense_full["workspace"]) == 0
 

@@ -26,7 +26,7 @@ from tests.tolerance import check
 
 pytestmark = pytest.mark.gpu
 
-NUM_VARIANTS = 11
+NUM_VARIANTS = 12
 M, N, K = 150, 392, 1536
 
 

@@ -46,7 +46,7 @@ def test_noalloc_matches_workspace_form_on_two_calls():
 
 def test_noalloc_refuses_shapes_beyond_its_scratch():
     dg = require_gpu()
-    m, n, k = 4096, 2112, 7168  # 256x256 tiles in equal K runs: 128 MiB of partials
+    m, n, k = 4096, 2816, 7168  # 256x256 tiles in equal K runs: 128 MiB of partials
     assert dg.dg_get_workspace_size(m, n, k, 1) > 33587200
     a = torch.zeros((m, k), dtype=torch.uint8, device="cuda")
     b = torch.zeros((n, k), dtype=torch.uint8, device="cuda")
