@@ -1298,9 +1298,11 @@ GemmConfig choose_config(int layout, int m, int n, int k, int groups, int num_cu
     // CUs but one round of 256 x 160 tiles fills at least 80% of them, the
     // narrower tile runs data-parallel in one wave (measured 4096 x 2112 x
     // 7168: 103.4 us against 113.6 us for 256 x 256 tiles in equal
-    // stream-K runs).
+    // stream-K runs).  Not for the masked layout, whose tile count is only
+    // a hint (4 x 1024 x 4096 x 7168 with about 512 valid rows per group:
+    // 177 us with 256 x 160 tiles against 133 us with 256 x 256).
     const int64_t t256 = tiles_of(256, 256), t160 = tiles_of(256, 160);
-    if (narrow_ok && !qout && layout != kKGrouped && 10 * t256 < 7 * (int64_t)num_cus && 5 * t160 >= 4 * (int64_t)num_cus && t160 <= num_cus) v = 11;
+    if (narrow_ok && !qout && (layout == kDense || layout == kContiguous) && 10 * t256 < 7 * (int64_t)num_cus && 5 * t160 >= 4 * (int64_t)num_cus && t160 <= num_cus) v = 11;
   } else {
     // Mid-size M (e.g. 1024 rows in all): 128-row tiles, 256 columns wide
     // unless 128 columns fill the CUs' last round better (measured on the

@@ -131,6 +131,9 @@ def test_stream_k_workspace_size():
     # tiles but 224 with 256 x 160 ones, which then run data-parallel.
     fields = dict(kv.split("=") for kv in dg.dg_describe_config(dg.LAYOUT_DENSE, 4096, 2112, 7168, 1, 256).split())
     assert (fields["bm"], fields["bn"], fields["stream_k"], fields["tiles"]) == ("256", "160", "0", "224")
+    # The masked layout's tile count is only a hint: it keeps 256 x 256.
+    fields = dict(kv.split("=") for kv in dg.dg_describe_config(dg.LAYOUT_MASKED, 1024, 4096, 7168, 4, 256, 512).split())
+    assert (fields["bm"], fields["bn"]) == ("256", "256")
     dense_full = dict(kv.split("=") for kv in dg.dg_describe_config(dg.LAYOUT_DENSE, 4096, 4096, 7168, 1, 256).split())
     assert int(dense_full["tiles"]) == 256 and int(dense_full["stream_k"]) == 0 and int(dense_full["workspace"]) == 0
 
