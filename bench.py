@@ -108,9 +108,9 @@ def parse_args(argv=None):
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work for the oracle sample")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain device copy of known size (for counter calibration)")
-    p.add_argument("--launches-only", metavar="WORKLOAD",
-                   help="only quantise and launch this workload's GEMM --reps times, no timing "
-                        "(the program rocprofv3 --pmc runs for the traffic counters)")
+    p.add_argument("--launches-only", metavar="WORKLOADS",
+                   help="only quantise and launch these comma-separated workloads' GEMMs --reps times each, in "
+                        "order, no timing (the program rocprofv3 --pmc runs for the counter summaries)")
     p.add_argument("--reps", type=int, default=5)
     p.add_argument("--write-mfma", metavar="PMC_CSV",
                    help="with --launches-only W: write profiles/gemm_kernel_W_mfma.txt from a counter pass "
@@ -556,54 +556,72 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def _counter_per_dispatch(path, counter, name_part):
+def _counter_values(path, counter, name_part):
+    """Per-dispatch values of one counter (summed over its instances) for the
+    kernels whose name contains name_part, in dispatch order."""
     import csv
     sums = {}
     with open(path) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] == counter and name_part in r["Kernel_Name"]:
-                sums[r["Dispatch_Id"]] = sums.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+                d = int(r["Dispatch_Id"])
+                sums[d] = sums.get(d, 0.0) + float(r["Counter_Value"])
     if not sums:
         raise SystemExit(f"no {counter} rows for kernels matching {name_part!r} in {path}")
-    return float(np.median(list(sums.values()))), len(sums)
+    return [sums[d] for d in sorted(sums)]
+
+
+def _per_workload(values, workloads, reps, what):
+    """Split dispatch-ordered values into the workloads' consecutive groups
+    of `reps` launches (bench.py --launches-only W1,W2,... launches each
+    workload's GEMM reps times, in order) and take each group's median."""
+    if len(values) != reps * len(workloads):
+        raise SystemExit(f"{what}: {len(values)} GEMM dispatches for {len(workloads)} workloads x {reps} launches")
+    return [(float(np.median(values[i * reps:(i + 1) * reps])), reps) for i in range(len(workloads))]
 
 
 def traffic_path(workload, scales="fp32"):
     return os.path.join(PROFILES, f"gemm_kernel_{workload}{'_ue8m0' if scales == 'ue8m0' else ''}_traffic.txt")
 
 
-def write_traffic(workload, scales, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
-    fetch, nf = _counter_per_dispatch(fetch_csv, "FETCH_SIZE", "gemm_kernel")
-    write, nw = _counter_per_dispatch(write_csv, "WRITE_SIZE", "gemm_kernel")
-    cfetch, _ = _counter_per_dispatch(copy_fetch_csv, "FETCH_SIZE", "copyBuffer")
-    cwrite, _ = _counter_per_dispatch(copy_write_csv, "WRITE_SIZE", "copyBuffer")
-    fscale, wscale = COPY_BYTES / (cfetch * 1024), COPY_BYTES / (cwrite * 1024)
-    traffic = fetch * 1024 * fscale + write * 1024 * wscale
+def _launch_cmd(workloads, scales, reps):
     sflag = " --scales ue8m0" if scales == "ue8m0" else ""
-    lines = [
-        f"workload={workload}",
-        f"scales={scales}",
-        f"kernel_source_sha256_16={kernel_source_hash()}",
-        f"fetch_kib_per_dispatch={fetch:.1f}  (median of {nf} dispatches)",
-        f"write_kib_per_dispatch={write:.1f}  (median of {nw} dispatches)",
-        f"copy_fetch_kib={cfetch:.1f}  copy_write_kib={cwrite:.1f}  (plain copy of {COPY_BYTES} bytes each way)",
-        f"fetch_scale={fscale:.4f}  write_scale={wscale:.4f}",
-        f"traffic_bytes_per_launch={traffic:.0f}",
-        "",
-        "commands (from the repository root, REPO = its absolute path):",
-        "  cd /tmp && export TMPDIR=/tmp",
-        "  rocprofv3 --pmc FETCH_SIZE -f csv -d $REPO/gpurun_out/pmc_copy_f -o p -- python3 $REPO/bench.py --calibrate-copy",
-        "  rocprofv3 --pmc WRITE_SIZE -f csv -d $REPO/gpurun_out/pmc_copy_w -o p -- python3 $REPO/bench.py --calibrate-copy",
-        f"  rocprofv3 --pmc FETCH_SIZE -f csv -d $REPO/gpurun_out/pmc_f -o p -- python3 $REPO/bench.py --launches-only {workload}{sflag}",
-        f"  rocprofv3 --pmc WRITE_SIZE -f csv -d $REPO/gpurun_out/pmc_w -o p -- python3 $REPO/bench.py --launches-only {workload}{sflag}",
-        f"  python3 bench.py --launches-only {workload}{sflag} --write-traffic gpurun_out/pmc_f/p_counter_collection.csv "
-        "gpurun_out/pmc_w/p_counter_collection.csv gpurun_out/pmc_copy_f/p_counter_collection.csv "
-        "gpurun_out/pmc_copy_w/p_counter_collection.csv",
-    ]
-    path = traffic_path(workload, scales)
-    with open(path, "w") as f:
-        f.write("\n".join(lines) + "\n")
-    print(path)
+    return f"$REPO/bench.py --launches-only {','.join(workloads)} --reps {reps}{sflag}"
+
+
+def write_traffic(workloads, scales, reps, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    fetch = _per_workload(_counter_values(fetch_csv, "FETCH_SIZE", "gemm_kernel"), workloads, reps, "FETCH_SIZE")
+    write = _per_workload(_counter_values(write_csv, "WRITE_SIZE", "gemm_kernel"), workloads, reps, "WRITE_SIZE")
+    cfetch = float(np.median(_counter_values(copy_fetch_csv, "FETCH_SIZE", "copyBuffer")))
+    cwrite = float(np.median(_counter_values(copy_write_csv, "WRITE_SIZE", "copyBuffer")))
+    fscale, wscale = COPY_BYTES / (cfetch * 1024), COPY_BYTES / (cwrite * 1024)
+    cmd = _launch_cmd(workloads, scales, reps)
+    for wl, (f_kib, nf), (w_kib, nw) in zip(workloads, fetch, write):
+        traffic = f_kib * 1024 * fscale + w_kib * 1024 * wscale
+        lines = [
+            f"workload={wl}",
+            f"scales={scales}",
+            f"kernel_source_sha256_16={kernel_source_hash()}",
+            f"fetch_kib_per_dispatch={f_kib:.1f}  (median of {nf} dispatches)",
+            f"write_kib_per_dispatch={w_kib:.1f}  (median of {nw} dispatches)",
+            f"copy_fetch_kib={cfetch:.1f}  copy_write_kib={cwrite:.1f}  (plain copy of {COPY_BYTES} bytes each way)",
+            f"fetch_scale={fscale:.4f}  write_scale={wscale:.4f}",
+            f"traffic_bytes_per_launch={traffic:.0f}",
+            "",
+            "commands (from the repository root, REPO = its absolute path):",
+            "  cd /tmp && export TMPDIR=/tmp",
+            "  rocprofv3 --pmc FETCH_SIZE -f csv -d $REPO/gpurun_out/pmc_copy_f -o p -- python3 $REPO/bench.py --calibrate-copy",
+            "  rocprofv3 --pmc WRITE_SIZE -f csv -d $REPO/gpurun_out/pmc_copy_w -o p -- python3 $REPO/bench.py --calibrate-copy",
+            f"  rocprofv3 --pmc FETCH_SIZE -f csv -d $REPO/gpurun_out/pmc_f -o p -- python3 {cmd}",
+            f"  rocprofv3 --pmc WRITE_SIZE -f csv -d $REPO/gpurun_out/pmc_w -o p -- python3 {cmd}",
+            f"  python3 {cmd.replace('$REPO/', '')} --write-traffic gpurun_out/pmc_f/p_counter_collection.csv "
+            "gpurun_out/pmc_w/p_counter_collection.csv gpurun_out/pmc_copy_f/p_counter_collection.csv "
+            "gpurun_out/pmc_copy_w/p_counter_collection.csv",
+        ]
+        path = traffic_path(wl, scales)
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print(path)
 
 
 MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_INSTS_VALU_MFMA_MOPS_F6F4 SQ_INSTS_MFMA "
@@ -615,36 +633,37 @@ def mfma_path(workload, scales="fp32"):
     return os.path.join(PROFILES, f"gemm_kernel_{workload}{'_ue8m0' if scales == 'ue8m0' else ''}_mfma.txt")
 
 
-def write_mfma(workload, scales, pmc_csv, num_cus):
-    """MFMA-busy fraction of one workload's GEMM launches from a counter pass:
-    SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) / (GRBM_GUI_ACTIVE per XCD x
-    SIMDs), medians over the dispatches; plus the MFMA op count against the
-    algorithmic flops."""
-    busy, nd = _counter_per_dispatch(pmc_csv, "SQ_VALU_MFMA_BUSY_CYCLES", "gemm_kernel")
-    gui, _ = _counter_per_dispatch(pmc_csv, "GRBM_GUI_ACTIVE", "gemm_kernel")
-    mops, _ = _counter_per_dispatch(pmc_csv, "SQ_INSTS_VALU_MFMA_MOPS_F8", "gemm_kernel")
+def write_mfma(workloads, scales, reps, pmc_csv, num_cus):
+    """MFMA-busy fraction of each workload's GEMM launches from one counter
+    pass: SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) / (GRBM_GUI_ACTIVE per
+    XCD x SIMDs), medians over the workload's dispatches; plus the MFMA op
+    count against the algorithmic flops."""
+    busy = _per_workload(_counter_values(pmc_csv, "SQ_VALU_MFMA_BUSY_CYCLES", "gemm_kernel"), workloads, reps, "busy")
+    gui = _per_workload(_counter_values(pmc_csv, "GRBM_GUI_ACTIVE", "gemm_kernel"), workloads, reps, "gui")
+    mops = _per_workload(_counter_values(pmc_csv, "SQ_INSTS_VALU_MFMA_MOPS_F8", "gemm_kernel"), workloads, reps, "mops")
     simds = 4 * num_cus
-    frac = busy / (gui / MI355X_XCDS * simds)
-    sflag = " --scales ue8m0" if scales == "ue8m0" else ""
-    lines = [
-        f"workload={workload}",
-        f"scales={scales}",
-        f"kernel_source_sha256_16={kernel_source_hash()}",
-        f"mfma_busy_cycles={busy:.6g}  (SQ_VALU_MFMA_BUSY_CYCLES, median of {nd} dispatches, all SIMDs)",
-        f"grbm_gui_active={gui:.6g}  (summed over {MI355X_XCDS} XCDs)",
-        f"simds={simds}",
-        f"mfma_busy_frac={frac:.4f}",
-        f"mfma_flops={mops * 512:.6g}  (SQ_INSTS_VALU_MFMA_MOPS_F8 x 512)",
-        "",
-        "commands (from the repository root, REPO = its absolute path):",
-        "  cd /tmp && export TMPDIR=/tmp",
-        f"  rocprofv3 --pmc {MFMA_COUNTERS} -f csv -d $REPO/gpurun_out/pmcm -o p -- python3 $REPO/bench.py --launches-only {workload}{sflag}",
-        f"  python3 bench.py --launches-only {workload}{sflag} --write-mfma gpurun_out/pmcm/p_counter_collection.csv",
-    ]
-    path = mfma_path(workload, scales)
-    with open(path, "w") as f:
-        f.write("\n".join(lines) + "\n")
-    print(path)
+    cmd = _launch_cmd(workloads, scales, reps)
+    for wl, (b, nd), (g, _), (mo, _) in zip(workloads, busy, gui, mops):
+        frac = b / (g / MI355X_XCDS * simds)
+        lines = [
+            f"workload={wl}",
+            f"scales={scales}",
+            f"kernel_source_sha256_16={kernel_source_hash()}",
+            f"mfma_busy_cycles={b:.6g}  (SQ_VALU_MFMA_BUSY_CYCLES, median of {nd} dispatches, all SIMDs)",
+            f"grbm_gui_active={g:.6g}  (summed over {MI355X_XCDS} XCDs)",
+            f"simds={simds}",
+            f"mfma_busy_frac={frac:.4f}",
+            f"mfma_flops={mo * 512:.6g}  (SQ_INSTS_VALU_MFMA_MOPS_F8 x 512)",
+            "",
+            "commands (from the repository root, REPO = its absolute path):",
+            "  cd /tmp && export TMPDIR=/tmp",
+            f"  rocprofv3 --pmc {MFMA_COUNTERS} -f csv -d $REPO/gpurun_out/pmcm -o p -- python3 {cmd}",
+            f"  python3 {cmd.replace('$REPO/', '')} --write-mfma gpurun_out/pmcm/p_counter_collection.csv",
+        ]
+        path = mfma_path(wl, scales)
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print(path)
 
 
 def _read_summary(path, key):
@@ -677,13 +696,13 @@ def main(argv=None):
     args = parse_args(argv)
     if args.write_traffic:
         if not args.launches_only:
-            raise SystemExit("--write-traffic needs --launches-only WORKLOAD")
-        write_traffic(args.launches_only, args.scales, *args.write_traffic)
+            raise SystemExit("--write-traffic needs --launches-only WORKLOADS")
+        write_traffic(args.launches_only.split(","), args.scales, args.reps, *args.write_traffic)
         return 0
     if args.write_mfma:
         if not args.launches_only:
-            raise SystemExit("--write-mfma needs --launches-only WORKLOAD")
-        write_mfma(args.launches_only, args.scales, args.write_mfma, args.num_cus)
+            raise SystemExit("--write-mfma needs --launches-only WORKLOADS")
+        write_mfma(args.launches_only.split(","), args.scales, args.reps, args.write_mfma, args.num_cus)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -706,13 +725,16 @@ def main(argv=None):
 
     if args.launches_only:
         import synth
-        wl = {w.name: w for w in synth.workloads() + synth.pages_workloads() + synth.extra_workloads()}[args.launches_only]
-        p = Prepared(dg, torch, wl, args.scales)
-        for r in range(args.reps):
-            p.quant(dg)
-            p.gemm(dg, r)
-        torch.cuda.synchronize()
-        print(json.dumps({"launches": args.reps, "workload": wl.name, "config": p.config}))
+        allw = {w.name: w for w in synth.workloads() + synth.pages_workloads() + synth.extra_workloads()}
+        for name in args.launches_only.split(","):
+            p = Prepared(dg, torch, allw[name], args.scales)
+            for r in range(args.reps):
+                p.quant(dg)
+                p.gemm(dg, r)
+            torch.cuda.synchronize()
+            print(json.dumps({"launches": args.reps, "workload": name, "config": p.config}), flush=True)
+            del p
+            torch.cuda.empty_cache()
         return 0
 
     if args.trace_child:

@@ -1016,6 +1016,34 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
             packed[i][j][1] = b1 | ((recv >> 16) << 16);
           }
         }
+      if (LAYOUT != kContiguous && !DQ) {
+        // Plain bf16 output: every lane stores its packed words straight from
+        // registers (rows r, r + 1 of two adjacent columns, 32-bit stores;
+        // the 8 lanes of a row write 32 contiguous bytes and the wave's 4
+        // fragments of a row fill whole 128-byte lines).  No LDS staging
+        // and no barrier, so the workgroup goes on to its next tile while
+        // the stores drain.  (The contiguous layout keeps the LDS-staged
+        // stores: its per-row expert checks here pushed the 256 x 256
+        // kernel to 69 spilled registers and 8% more time.)
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int row = m0 + wm * T::TM + i * 16 + 4 * kg + (odd ? 2 : 0) + h;
+            if (row >= rows_valid) continue;
+            uint16_t* drow = D + (int64_t)row * p.ldd;
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j) {
+              const int col = n0 + wn * T::TN + j * 16 + (fr & ~1);
+              if (col + 1 < p.n) {
+                *reinterpret_cast<uint32_t*>(drow + col) = packed[i][j][h];
+              } else if (col < p.n) {
+                drow[col] = (uint16_t)(packed[i][j][h] & 0xFFFFu);
+              }
+            }
+          }
+        continue;  // next work unit (or pass)
+      }
 #pragma unroll
       for (int er = 0; er < T::BM / kER; ++er) {
         lds_barrier();  // LDS free: the K loop (or previous pass) is done reading

@@ -67,3 +67,35 @@ def test_library_tile_count_matches_the_example():
     finally:
         del os.environ["DG_FORCE_CONFIG"]
     assert "bm=128 bn=128" in desc and "tiles=112" in desc
+
+
+def test_counter_summaries_split_dispatches_per_workload(tmp_path, monkeypatch):
+    # One rocprofv3 --pmc pass over bench.py --launches-only W1,W2 --reps 3
+    # sees 6 GEMM dispatches in order; each workload's summary takes the
+    # median of its own 3, scaled by the copy calibration.
+    import csv
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+
+    def write_csv(path, counter, kernel, values):
+        with open(path, "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            for d, v in enumerate(values, start=10):
+                for part in (0.25, 0.75):  # two counter instances per dispatch, summed
+                    w.writerow({"Dispatch_Id": d, "Kernel_Name": kernel, "Counter_Name": counter, "Counter_Value": v * part})
+                w.writerow({"Dispatch_Id": d + 100, "Kernel_Name": "quant_1x128_kernel", "Counter_Name": counter,
+                            "Counter_Value": 1e9})
+
+    f, wr, cf, cw = (str(tmp_path / n) for n in ("f.csv", "w.csv", "cf.csv", "cw.csv"))
+    write_csv(f, "FETCH_SIZE", "gemm_kernel<x>", [100, 300, 200, 1000, 1200, 1100])
+    write_csv(wr, "WRITE_SIZE", "gemm_kernel<x>", [10, 10, 10, 50, 50, 50])
+    write_csv(cf, "FETCH_SIZE", "__amd_rocclr_copyBuffer", [bench.COPY_BYTES / 1024 / 2])
+    write_csv(cw, "WRITE_SIZE", "__amd_rocclr_copyBuffer", [bench.COPY_BYTES / 1024])
+    bench.write_traffic(["w1", "w2"], "fp32", 3, f, wr, cf, cw)
+    got = {}
+    for wl in ("w1", "w2"):
+        fields = dict(line.split("=", 1) for line in open(bench.traffic_path(wl)) if "=" in line and not line.startswith(" "))
+        got[wl] = float(fields["traffic_bytes_per_launch"].split()[0])
+    assert got == {"w1": (200 * 2 + 10) * 1024, "w2": (1100 * 2 + 50) * 1024}
+    with pytest.raises(SystemExit):
+        bench.write_traffic(["w1", "w2", "w3"], "fp32", 3, f, wr, cf, cw)
