@@ -918,8 +918,18 @@ def shape_record(p, t_events, quant_ms, median_us=None):
         "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "scale_bytes": p.sf_bytes,
         "quant_1x128_us": round(quant_ms * 1e3, 3),
+        "traffic_bytes": _round_or_none(read_traffic(p.wl.name, p.scales)),
+        "mfma_busy_frac": _round_or_none(read_mfma_busy(p.wl.name, p.scales), 4),
         "config": p.config,
     }
+
+
+def _round_or_none(x, nd=0):
+    """Counter-summary figure for the record: None when there is no summary
+    taken with the current kernel sources."""
+    if x is None:
+        return None
+    return round(x, nd) if nd else round(x)
 
 
 if __name__ == "__main__":
