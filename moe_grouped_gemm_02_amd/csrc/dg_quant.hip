@@ -14,18 +14,23 @@
 
 namespace dg {
 
-// 1x128 activation tiles.  Block (x, y) covers tiles [32 x, 32 x + 32) of the
-// rows y, y + gridDim.y, ...; 8 consecutive lanes own one tile, 16 bf16
-// values (32 bytes) each, so a wave reads 2 KB of one row.
-constexpr int kQTilesPerBlock = 32;
+// 1x128 activation tiles.  A block is one wave: block (x, y) covers tiles
+// [8 x, 8 x + 8) of rows kQRows y, kQRows y + 1, ... and then every
+// kQRows gridDim.y rows further down; 8 consecutive lanes own one tile, 16
+// bf16 values (32 bytes) each, so a load reads 2 KB of one row.  The wave
+// issues the loads of its kQRows rows before quantising any of them: with
+// one row's 32 bytes per lane in flight the stream ran at 4.6 TB/s on
+// 32768 x 7168, with four rows' at 5.2 TB/s.
+constexpr int kQTilesPerBlock = 8;
+constexpr int kQRows = 4;
 
 // POW2: scales are UE8M0 exponents (one byte each) instead of fp32 values;
 // the scale matrices have the same [(G)][C/128][ld] shape either way.
 template <bool POW2>
-__global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __restrict__ x,
-                                                          uint8_t* __restrict__ q,
-                                                          void* __restrict__ sf_out, int rows,
-                                                          int cols, int64_t ld_sf, int groups) {
+__global__ __launch_bounds__(64) void quant_1x128_kernel(const uint16_t* __restrict__ x,
+                                                         uint8_t* __restrict__ q,
+                                                         void* __restrict__ sf_out, int rows,
+                                                         int cols, int64_t ld_sf, int groups) {
   float* sf = static_cast<float*>(sf_out);
   uint8_t* sf8 = static_cast<uint8_t*>(sf_out);
   const int tiles_per_row = cols / kBlockK;
@@ -33,37 +38,49 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const uint16_t* __rest
   const int sub = threadIdx.x & 7;  // lane within the tile's 8-lane group
   const int j = blockIdx.x * kQTilesPerBlock + (threadIdx.x >> 3);
   if (j < tiles_per_row) {
-    for (int gr = blockIdx.y; gr < total_rows; gr += gridDim.y) {  // gr = g * rows + r
-      const int g = gr / rows, r = gr - g * rows;
-      const int64_t elem = (int64_t)gr * cols + j * kBlockK + sub * 16;
-      const uint4 lo = *reinterpret_cast<const uint4*>(x + elem);
-      const uint4 hi = *reinterpret_cast<const uint4*>(x + elem + 8);
-      const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      float amax = 0.0f;
+    for (int gr0 = blockIdx.y * kQRows; gr0 < total_rows; gr0 += gridDim.y * kQRows) {  // gr = g * rows + r
+      uint4 lo[kQRows], hi[kQRows];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w[i] & 0xFFFFu)), fabsf(bf16_bits_to_f32(w[i] >> 16))));
-#pragma unroll
-      for (int off = 4; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 8));
-      uint32_t out[4];
-      const int64_t sf_at = ((int64_t)g * tiles_per_row + j) * ld_sf + r;
-      if constexpr (POW2) {
-        const uint32_t e = ue8m0_exponent(amax);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          out[i] = e4m3_x4(pow2_quotient(w[2 * i] & 0xFFFFu, e), pow2_quotient(w[2 * i] >> 16, e),
-                           pow2_quotient(w[2 * i + 1] & 0xFFFFu, e), pow2_quotient(w[2 * i + 1] >> 16, e));
-        if (sub == 0) sf8[sf_at] = (uint8_t)e;
-      } else {
-        const float s = amax / 448.0f;
-        const double rcp = tile_reciprocal(s);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          out[i] = e4m3_x4(quotient(w[2 * i] & 0xFFFFu, rcp), quotient(w[2 * i] >> 16, rcp),
-                           quotient(w[2 * i + 1] & 0xFFFFu, rcp), quotient(w[2 * i + 1] >> 16, rcp));
-        if (sub == 0) sf[sf_at] = s;
+      for (int u = 0; u < kQRows; ++u) {
+        // Rows past the end reload the last row; their results are dropped.
+        const int64_t elem = (int64_t)min(gr0 + u, total_rows - 1) * cols + j * kBlockK + sub * 16;
+        lo[u] = *reinterpret_cast<const uint4*>(x + elem);
+        hi[u] = *reinterpret_cast<const uint4*>(x + elem + 8);
       }
-      *reinterpret_cast<uint4*>(q + elem) = make_uint4(out[0], out[1], out[2], out[3]);
+#pragma unroll
+      for (int u = 0; u < kQRows; ++u) {
+        const int gr = gr0 + u;
+        const int g = gr / rows, r = gr - g * rows;
+        const uint32_t w[8] = {lo[u].x, lo[u].y, lo[u].z, lo[u].w, hi[u].x, hi[u].y, hi[u].z, hi[u].w};
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w[i] & 0xFFFFu)), fabsf(bf16_bits_to_f32(w[i] >> 16))));
+#pragma unroll
+        for (int off = 4; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 8));
+        uint32_t out[4];
+        const int64_t sf_at = ((int64_t)g * tiles_per_row + j) * ld_sf + r;
+        const bool live = gr < total_rows;
+        if constexpr (POW2) {
+          const uint32_t e = ue8m0_exponent(amax);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            out[i] = e4m3_x4(pow2_quotient(w[2 * i] & 0xFFFFu, e), pow2_quotient(w[2 * i] >> 16, e),
+                             pow2_quotient(w[2 * i + 1] & 0xFFFFu, e), pow2_quotient(w[2 * i + 1] >> 16, e));
+          if (live && sub == 0) sf8[sf_at] = (uint8_t)e;
+        } else {
+          const float s = amax / 448.0f;
+          const double rcp = tile_reciprocal(s);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            out[i] = e4m3_x4(quotient(w[2 * i] & 0xFFFFu, rcp), quotient(w[2 * i] >> 16, rcp),
+                             quotient(w[2 * i + 1] & 0xFFFFu, rcp), quotient(w[2 * i + 1] >> 16, rcp));
+          if (live && sub == 0) sf[sf_at] = s;
+        }
+        if (live)
+          *reinterpret_cast<uint4*>(q + (int64_t)gr * cols + j * kBlockK + sub * 16) =
+              make_uint4(out[0], out[1], out[2], out[3]);
+      }
     }
   }
   // Padding entries of the scale matrix (rows in [rows, ld_sf)) are zero.
@@ -241,16 +258,17 @@ hipError_t launch_quant_1x128(const uint16_t* x, uint8_t* q, void* sf, int rows,
   const int tiles_per_row = cols / kBlockK;
   const int gx = (tiles_per_row + kQTilesPerBlock - 1) / kQTilesPerBlock;
   const int64_t total_rows = (int64_t)groups * rows;
-  // About 8 blocks per CU; every block walks its column of tiles down the rows.
-  int64_t gy = (2048 + gx - 1) / gx;
-  if (gy > total_rows) gy = total_rows;
+  // About 8192 one-wave blocks (32 per CU); every block walks its column of
+  // tiles down the rows, kQRows at a time.
+  int64_t gy = (8192 + gx - 1) / gx;
+  if (gy > (total_rows + kQRows - 1) / kQRows) gy = (total_rows + kQRows - 1) / kQRows;
   if (gy > 65535) gy = 65535;
   if (gy < 1) gy = 1;
   const dim3 grid(gx > 0 ? gx : 1, (unsigned)gy);
   if (pow2)
-    hipLaunchKernelGGL(quant_1x128_kernel<true>, grid, dim3(256), 0, stream, x, q, sf, rows, cols, ld_sf, groups);
+    hipLaunchKernelGGL(quant_1x128_kernel<true>, grid, dim3(64), 0, stream, x, q, sf, rows, cols, ld_sf, groups);
   else
-    hipLaunchKernelGGL(quant_1x128_kernel<false>, grid, dim3(256), 0, stream, x, q, sf, rows, cols, ld_sf, groups);
+    hipLaunchKernelGGL(quant_1x128_kernel<false>, grid, dim3(64), 0, stream, x, q, sf, rows, cols, ld_sf, groups);
   return hipGetLastError();
 }
 
