@@ -991,8 +991,12 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
       // bf16 (RNE) tile staged through LDS, then stored as 16-byte row chunks.
       // A lane holds column fr of rows 4kg..4kg+3 of each fragment; lane pairs
       // (fr, fr^1) swap halves so each lane writes two rows of two adjacent
-      // columns as 32-bit words.
-      constexpr int kRowBytes = T::BN * 2 + 32;
+      // columns as 32-bit words.  Staged rows are padded by 16 bytes: the 8
+      // rows of one 32-bit write instruction then start 8 banks apart (no
+      // conflicts for BN = 64, 128, 160, 256), and the whole 256 x 256 tile
+      // fits the two stages' 132 KB, so it is written in one pass (with 32
+      // bytes of padding it took two 128-row passes and two more barriers).
+      constexpr int kRowBytes = T::BN * 2 + 16;
       constexpr int kER = (T::BM * kRowBytes <= T::STAGES * T::kStageBytes) ? T::BM : T::TM;
       static_assert(kER * kRowBytes <= T::STAGES * T::kStageBytes, "epilogue tile does not fit");
       static_assert(kER == T::BM || kER == T::TM, "epilogue pass must be whole wave rows");
