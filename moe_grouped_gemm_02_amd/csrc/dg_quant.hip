@@ -14,41 +14,45 @@
 
 namespace dg {
 
-// 1x128 activation tiles.  A block is one wave: block (x, y) covers tiles
-// [8 x, 8 x + 8) of rows kQRows y, kQRows y + 1, ... and then every
-// kQRows gridDim.y rows further down; 8 consecutive lanes own one tile, 16
-// bf16 values (32 bytes) each, so a load reads 2 KB of one row.  The wave
-// issues the loads of its kQRows rows before quantising any of them: with
-// one row's 32 bytes per lane in flight the stream ran at 4.6 TB/s on
-// 32768 x 7168, with four rows' at 5.2 TB/s.
-constexpr int kQTilesPerBlock = 8;
-constexpr int kQRows = 4;
+// 1x128 activation tiles.  Each wave owns 8 tiles of a row (8 consecutive
+// lanes per tile, 16 bf16 values = 32 bytes each, so a load reads 2 KB of
+// one row) and walks down the rows U at a time, issuing the loads of its U
+// rows before quantising any of them.  Block (x, y) holds 4 waves: tiles
+// [8 x, 8 x + 8), wave w starting at row (4 y + w) U, then every
+// 4 U gridDim.y rows further down.  U trades bytes in flight against the
+// serial work of a wave: 4 on tall matrices (32768 x 7168: 132 us, against
+// 142 us with one row per trip), 2 on 4096-row ones, 1 on decode-sized ones,
+// where four rows quantised one after another added 0.7 us to a 2.7 us call.
+constexpr int kQTilesPerWave = 8;
+constexpr int kQWaves = 4;
 
 // POW2: scales are UE8M0 exponents (one byte each) instead of fp32 values;
 // the scale matrices have the same [(G)][C/128][ld] shape either way.
-template <bool POW2>
-__global__ __launch_bounds__(64) void quant_1x128_kernel(const uint16_t* __restrict__ x,
-                                                         uint8_t* __restrict__ q,
-                                                         void* __restrict__ sf_out, int rows,
-                                                         int cols, int64_t ld_sf, int groups) {
+template <bool POW2, int U>
+__global__ __launch_bounds__(64 * kQWaves) void quant_1x128_kernel(const uint16_t* __restrict__ x,
+                                                                   uint8_t* __restrict__ q,
+                                                                   void* __restrict__ sf_out, int rows,
+                                                                   int cols, int64_t ld_sf, int groups) {
   float* sf = static_cast<float*>(sf_out);
   uint8_t* sf8 = static_cast<uint8_t*>(sf_out);
   const int tiles_per_row = cols / kBlockK;
   const int total_rows = groups * rows;
   const int sub = threadIdx.x & 7;  // lane within the tile's 8-lane group
-  const int j = blockIdx.x * kQTilesPerBlock + (threadIdx.x >> 3);
+  const int j = blockIdx.x * kQTilesPerWave + ((threadIdx.x & 63) >> 3);
+  const int wave = threadIdx.x >> 6;
   if (j < tiles_per_row) {
-    for (int gr0 = blockIdx.y * kQRows; gr0 < total_rows; gr0 += gridDim.y * kQRows) {  // gr = g * rows + r
-      uint4 lo[kQRows], hi[kQRows];
+    const int step = gridDim.y * kQWaves * U;
+    for (int gr0 = (blockIdx.y * kQWaves + wave) * U; gr0 < total_rows; gr0 += step) {  // gr = g * rows + r
+      uint4 lo[U], hi[U];
 #pragma unroll
-      for (int u = 0; u < kQRows; ++u) {
+      for (int u = 0; u < U; ++u) {
         // Rows past the end reload the last row; their results are dropped.
         const int64_t elem = (int64_t)min(gr0 + u, total_rows - 1) * cols + j * kBlockK + sub * 16;
         lo[u] = *reinterpret_cast<const uint4*>(x + elem);
         hi[u] = *reinterpret_cast<const uint4*>(x + elem + 8);
       }
 #pragma unroll
-      for (int u = 0; u < kQRows; ++u) {
+      for (int u = 0; u < U; ++u) {
         const int gr = gr0 + u;
         const int g = gr / rows, r = gr - g * rows;
         const uint32_t w[8] = {lo[u].x, lo[u].y, lo[u].z, lo[u].w, hi[u].x, hi[u].y, hi[u].z, hi[u].w};
@@ -256,19 +260,30 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const uint16_t* __re
 hipError_t launch_quant_1x128(const uint16_t* x, uint8_t* q, void* sf, int rows, int cols,
                               int64_t ld_sf, int groups, bool pow2, hipStream_t stream) {
   const int tiles_per_row = cols / kBlockK;
-  const int gx = (tiles_per_row + kQTilesPerBlock - 1) / kQTilesPerBlock;
+  const int gx = (tiles_per_row + kQTilesPerWave - 1) / kQTilesPerWave;
   const int64_t total_rows = (int64_t)groups * rows;
-  // About 8192 one-wave blocks (32 per CU); every block walks its column of
-  // tiles down the rows, kQRows at a time.
-  int64_t gy = (8192 + gx - 1) / gx;
-  if (gy > (total_rows + kQRows - 1) / kQRows) gy = (total_rows + kQRows - 1) / kQRows;
+  // Rows per trip and waves in flight by height (measured on 64 .. 32768
+  // rows of 512 .. 16384 columns).
+  const int u = total_rows >= 16384 ? 4 : total_rows >= 2048 ? 2 : 1;
+  const int64_t waves = total_rows >= 16384 ? 16384 : 8192;
+  int64_t gy = (waves / kQWaves + gx - 1) / gx;
+  const int64_t need = (total_rows + (int64_t)kQWaves * u - 1) / ((int64_t)kQWaves * u);
+  if (gy > need) gy = need;
   if (gy > 65535) gy = 65535;
   if (gy < 1) gy = 1;
-  const dim3 grid(gx > 0 ? gx : 1, (unsigned)gy);
-  if (pow2)
-    hipLaunchKernelGGL(quant_1x128_kernel<true>, grid, dim3(64), 0, stream, x, q, sf, rows, cols, ld_sf, groups);
-  else
-    hipLaunchKernelGGL(quant_1x128_kernel<false>, grid, dim3(64), 0, stream, x, q, sf, rows, cols, ld_sf, groups);
+  const dim3 grid(gx > 0 ? gx : 1, (unsigned)gy), block(64 * kQWaves);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, x, q, sf, rows, cols, ld_sf, groups);
+  };
+  if (pow2) {
+    if (u == 4) go(quant_1x128_kernel<true, 4>);
+    else if (u == 2) go(quant_1x128_kernel<true, 2>);
+    else go(quant_1x128_kernel<true, 1>);
+  } else {
+    if (u == 4) go(quant_1x128_kernel<false, 4>);
+    else if (u == 2) go(quant_1x128_kernel<false, 2>);
+    else go(quant_1x128_kernel<false, 1>);
+  }
   return hipGetLastError();
 }
 
