@@ -26,6 +26,20 @@ def test_quant_1x128_bit_exact(rows, cols):
     assert _same_f32(host(sf), rsf)
 
 
+# Heights around the quantiser's rows-per-trip thresholds (one row per trip
+# below 2048 rows, two from 2048, four from 16384), with ragged last trips,
+# and a grouped matrix whose group boundaries fall inside a four-row trip.
+@pytest.mark.parametrize("shape", [(2047, 256), (2051, 384), (16383, 128), (16395, 256), (3, 5467, 128)])
+def test_quant_1x128_tall_bit_exact(shape):
+    dg = require_gpu()
+    x = bf16_normal(shape, seed=510 + shape[-2])
+    ld = 5480 if len(shape) == 3 else None
+    q, sf = gpu_quant_1x128(dg, x, ld=ld)
+    rq, rsf = quant.quant_1x128(x, ld_sf=ld) if ld else quant.quant_1x128(x)
+    assert np.array_equal(host(q), rq)
+    assert _same_f32(host(sf), rsf)
+
+
 def test_quant_1x128_grouped_and_wide_ld():
     dg = require_gpu()
     x = bf16_normal((3, 37, 256), seed=77)

@@ -50,6 +50,19 @@ def test_quant_1x128_ue8m0_bit_exact(rows, cols):
     assert np.array_equal(host(sf), rsf)
 
 
+# Heights around the quantiser's rows-per-trip thresholds, ragged last trips,
+# and group boundaries inside a four-row trip.
+@pytest.mark.parametrize("shape", [(2051, 384), (16395, 256), (3, 5467, 128)])
+def test_quant_1x128_ue8m0_tall_bit_exact(shape):
+    dg = require_gpu()
+    x = bf16_normal(shape, seed=610 + shape[-2])
+    ld = 5480 if len(shape) == 3 else None
+    q, sf = gpu_quant_1x128_ue8m0(dg, x, ld=ld)
+    rq, rsf = ue8m0.quant_1x128_ue8m0(x, ld_sf=ld) if ld else ue8m0.quant_1x128_ue8m0(x)
+    assert np.array_equal(host(q), rq)
+    assert np.array_equal(host(sf), rsf)
+
+
 def test_quant_1x128_ue8m0_grouped_and_wide_ld():
     dg = require_gpu()
     x = bf16_normal((3, 37, 256), seed=78)
