@@ -331,6 +331,21 @@ template <class T, int LAYOUT, bool SK, int SF, int MAJ = 0>
 __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedule s) {
   static_assert(MAJ == 0 || (LAYOUT == kDense && SF != kScaleRowB), "MN-major operands: dense layout");
   constexpr bool kAT = (MAJ & kAMajorMN) != 0, kBT = (MAJ & kBMajorMN) != 0;
+  // Transposed fragments: the MFMA takes the B fragment as its first operand,
+  // so a lane's four results are one output row (row fr of the A fragment)
+  // and four consecutive columns 4 kg .. 4 kg + 3.  The row's activation
+  // scale is then one value per lane and fragment row, and the four bf16
+  // results are 8 contiguous bytes.  Per-column B scales (the K-grouped
+  // GEMM) keep the untransposed form, where a lane holds one column.
+  constexpr bool kTr = SF != kScaleRowB;
+  // One 16x16x128 product of fragments a (16 rows of A) and b (16 rows of B).
+  auto slice_mma = [](const v8i& a, const v8i& b) { return kTr ? mfma_fp8_slice(b, a) : mfma_fp8_slice(a, b); };
+  // The same with power-of-two scales inside the MFMA: ea for a's rows, eb
+  // for b's rows (one exponent byte per lane, for its row l mod 16).
+  auto scaled_mma = [](const v8i& a, int ea, const v8i& b, int eb, const v4f& c) {
+    return kTr ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, 0, 0, eb, 0, ea)
+               : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
+  };
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::STAGES * T::kStageBytes];
   __shared__ int last_flag;
 
@@ -724,8 +739,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
               }
               static_for<T::FN>([&](auto jc) {
                 constexpr int j = decltype(jc)::value;
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_cur, bfrag[j], acc[i][j], 0, 0, 0,
-                                                                             e_cur, 0, sbe[j]);
+                acc[i][j] = scaled_mma(a_cur, e_cur, bfrag[j], sbe[j], acc[i][j]);
                 if constexpr (i == T::FM - 1) {
                   // Keep the compiler from hoisting the load above the MFMA
                   // that still reads the register it overwrites.
@@ -794,8 +808,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
               }
   #pragma unroll
               for (int j = 0; j < T::FN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_cur, bfrag[j], acc[i][j], 0, 0, 0, e_cur,
-                                                                             0, sbe[j]);
+                acc[i][j] = scaled_mma(a_cur, e_cur, bfrag[j], sbe[j], acc[i][j]);
               if constexpr (T::kSpreadRows > 0) {
                 if (refill) issue_row(kb_next, buf_next, ic);
               }
@@ -828,15 +841,22 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
             // FMAs of row i, so the matrix core and the VALU overlap instead of
             // each FMA waiting on the MFMA just issued.
             auto load_a = [&](int i) { return frag_a(st, i); };
+            // Activation scales of fragment row i for this lane: its row fr
+            // (transposed fragments) or rows 4 kg .. 4 kg + 3.
             auto load_s = [&](int i) {
-              return *reinterpret_cast<const float4*>(st + T::kSOff + (wm * T::TM + i * 16 + 4 * kg) * 4);
+              if constexpr (kTr) {
+                const float v = *reinterpret_cast<const float*>(st + T::kSOff + (wm * T::TM + i * 16 + fr) * 4);
+                return make_float4(v, v, v, v);
+              } else {
+                return *reinterpret_cast<const float4*>(st + T::kSOff + (wm * T::TM + i * 16 + 4 * kg) * 4);
+              }
             };
             v4f part[T::kPipe ? 2 : 1][T::FN];
             v8i afrag = load_a(0);
             float4 s4 = load_s(0);
             if (T::kPipe) {
   #pragma unroll
-              for (int j = 0; j < T::FN; ++j) part[0][j] = mfma_fp8_slice(afrag, bfrag[j]);
+              for (int j = 0; j < T::FN; ++j) part[0][j] = slice_mma(afrag, bfrag[j]);
             }
             static_for<T::FM>([&](auto ic) {
               constexpr int i = decltype(ic)::value;
@@ -847,7 +867,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
                   afrag = load_a(i + 1);
                   s4 = load_s(i + 1);
   #pragma unroll
-                  for (int j = 0; j < T::FN; ++j) part[cur ^ 1][j] = mfma_fp8_slice(afrag, bfrag[j]);
+                  for (int j = 0; j < T::FN; ++j) part[cur ^ 1][j] = slice_mma(afrag, bfrag[j]);
                 }
               } else {
                 // MFMAs of row i, then the LDS reads of row i + 1, which complete
@@ -863,7 +883,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
                   __builtin_amdgcn_sched_barrier(0);
                 }
   #pragma unroll
-                for (int j = 0; j < T::FN; ++j) part[0][j] = mfma_fp8_slice(afrag, bfrag[j]);
+                for (int j = 0; j < T::FN; ++j) part[0][j] = slice_mma(afrag, bfrag[j]);
                 if constexpr (kPrio) {
                   __builtin_amdgcn_sched_barrier(0);
                   __builtin_amdgcn_s_setprio(0);
@@ -876,15 +896,26 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
               if constexpr (T::kSpreadRows > 0) {
                 if (refill) issue_row(kb_next, buf_next, ic);
               }
-              const float sa[4] = {s_cur.x, s_cur.y, s_cur.z, s_cur.w};
-              float sc[4];
+              if constexpr (kTr) {
+                // One row per lane: one scale for all four results of a fragment.
+                const float sc = kOneSB ? s_cur.x * sbw : 0.0f;
   #pragma unroll
-              for (int e = 0; e < 4; ++e) sc[e] = kOneSB ? sa[e] * sbw : 0.0f;
+                for (int j = 0; j < T::FN; ++j) {
+                  const float scj = kOneSB ? sc : s_cur.x * sbv[j];
   #pragma unroll
-              for (int j = 0; j < T::FN; ++j)
+                  for (int e = 0; e < 4; ++e) acc[i][j][e] = fmaf(part[cur][j][e], scj, acc[i][j][e]);
+                }
+              } else {
+                const float sa[4] = {s_cur.x, s_cur.y, s_cur.z, s_cur.w};
+                float sc[4];
   #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                  acc[i][j][e] = fmaf(part[cur][j][e], kOneSB ? sc[e] : sa[e] * sbv[j], acc[i][j][e]);
+                for (int e = 0; e < 4; ++e) sc[e] = kOneSB ? sa[e] * sbw : 0.0f;
+  #pragma unroll
+                for (int j = 0; j < T::FN; ++j)
+  #pragma unroll
+                  for (int e = 0; e < 4; ++e)
+                    acc[i][j][e] = fmaf(part[cur][j][e], kOneSB ? sc[e] : sa[e] * sbv[j], acc[i][j][e]);
+              }
             });
           }
         }
@@ -988,14 +1019,16 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
       }
 
       // ------------------------------------------------------------ epilogue
-      // bf16 (RNE) tile staged through LDS, then stored as 16-byte row chunks.
-      // A lane holds column fr of rows 4kg..4kg+3 of each fragment; lane pairs
-      // (fr, fr^1) swap halves so each lane writes two rows of two adjacent
-      // columns as 32-bit words.  Staged rows are padded by 16 bytes: the 8
-      // rows of one 32-bit write instruction then start 8 banks apart (no
-      // conflicts for BN = 64, 128, 160, 256), and the whole 256 x 256 tile
-      // fits the two stages' 132 KB, so it is written in one pass (with 32
-      // bytes of padding it took two 128-row passes and two more barriers).
+      // bf16 (RNE) results, stored from registers or staged through LDS and
+      // stored as 16-byte row chunks.  Transposed fragments: a lane holds row
+      // fr, columns 4kg..4kg+3 of each fragment, written as one 8-byte word
+      // pair.  Otherwise a lane holds column fr of rows 4kg..4kg+3, and lane
+      // pairs (fr, fr^1) swap halves so each lane writes two rows of two
+      // adjacent columns as 32-bit words.  Staged rows are padded by 16 bytes:
+      // the rows of one write instruction then start on different banks, and
+      // the whole 256 x 256 tile fits the two stages' 132 KB, so it is written
+      // in one pass (with 32 bytes of padding it took two 128-row passes and
+      // two more barriers).
       constexpr int kRowBytes = T::BN * 2 + 16;
       constexpr int kER = (T::BM * kRowBytes <= T::STAGES * T::kStageBytes) ? T::BM : T::TM;
       static_assert(kER * kRowBytes <= T::STAGES * T::kStageBytes, "epilogue tile does not fit");
@@ -1010,6 +1043,11 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
         for (int j = 0; j < T::FN; ++j) {
           const uint32_t b0 = f32_to_bf16_rne(acc[i][j][0]), b1 = f32_to_bf16_rne(acc[i][j][1]);
           const uint32_t b2 = f32_to_bf16_rne(acc[i][j][2]), b3 = f32_to_bf16_rne(acc[i][j][3]);
+          if constexpr (kTr) {  // columns 4kg, 4kg+1 | 4kg+2, 4kg+3 of row fr
+            packed[i][j][0] = b0 | (b1 << 16);
+            packed[i][j][1] = b2 | (b3 << 16);
+            continue;
+          }
           const uint32_t send = odd ? (b0 | (b1 << 16)) : (b2 | (b3 << 16));
           const uint32_t recv = (uint32_t)__shfl_xor((int)send, 1, 64);
           if (odd) {  // rows 4kg+2, 4kg+3; columns fr-1, fr
@@ -1029,6 +1067,29 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
         // the stores drain.  (The contiguous layout keeps the LDS-staged
         // stores: its per-row expert checks here pushed the 256 x 256
         // kernel to 69 spilled registers and 8% more time.)
+        if constexpr (kTr) {
+          // One 8-byte store per fragment: row fr, columns 4kg .. 4kg + 3
+          // (the 4 lanes of a row write 32 contiguous bytes, the wave's 4
+          // fragments of a row whole 128-byte lines).
+#pragma unroll
+          for (int i = 0; i < T::FM; ++i) {
+            const int row = m0 + wm * T::TM + i * 16 + fr;
+            if (row >= rows_valid) continue;
+            uint16_t* drow = D + (int64_t)row * p.ldd;
+#pragma unroll
+            for (int j = 0; j < T::FN; ++j) {
+              const int col = n0 + wn * T::TN + j * 16 + 4 * kg;
+              if (col + 3 < p.n) {
+                *reinterpret_cast<uint2*>(drow + col) = make_uint2(packed[i][j][0], packed[i][j][1]);
+              } else {
+#pragma unroll
+                for (int e = 0; e < 3; ++e)
+                  if (col + e < p.n) drow[col + e] = (uint16_t)(packed[i][j][e >> 1] >> ((e & 1) * 16));
+              }
+            }
+          }
+          continue;  // next work unit (or pass)
+        }
 #pragma unroll
         for (int i = 0; i < T::FM; ++i)
 #pragma unroll
@@ -1057,11 +1118,17 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
           for (int i = 0; i < T::FM; ++i)
 #pragma unroll
             for (int j = 0; j < T::FN; ++j) {
-              const int r = rbase + i * 16 + 4 * kg + (odd ? 2 : 0);
-              const int c = wn * T::TN + j * 16 + (fr & ~1);
-              uint8_t* dst = smem + r * kRowBytes + c * 2;
-              *reinterpret_cast<uint32_t*>(dst) = packed[i][j][0];
-              *reinterpret_cast<uint32_t*>(dst + kRowBytes) = packed[i][j][1];
+              if constexpr (kTr) {
+                const int r = rbase + i * 16 + fr;
+                const int c = wn * T::TN + j * 16 + 4 * kg;
+                *reinterpret_cast<uint2*>(smem + r * kRowBytes + c * 2) = make_uint2(packed[i][j][0], packed[i][j][1]);
+              } else {
+                const int r = rbase + i * 16 + 4 * kg + (odd ? 2 : 0);
+                const int c = wn * T::TN + j * 16 + (fr & ~1);
+                uint8_t* dst = smem + r * kRowBytes + c * 2;
+                *reinterpret_cast<uint32_t*>(dst) = packed[i][j][0];
+                *reinterpret_cast<uint32_t*>(dst + kRowBytes) = packed[i][j][1];
+              }
             }
         }
         lds_barrier();
