@@ -115,7 +115,10 @@ def parse_args(argv=None):
     p.add_argument("--write-mfma", metavar="PMC_CSV",
                    help="with --launches-only W: write profiles/gemm_kernel_W_mfma.txt from a counter pass "
                         "over the MFMA counters (see write_mfma)")
-    p.add_argument("--num-cus", type=int, default=256, help="CUs of the measured GPU, for --write-mfma")
+    p.add_argument("--write-stalls", nargs=2, metavar=("PMC_CSV_A", "PMC_CSV_B"),
+                   help="with --launches-only W: write profiles/gemm_kernel_W_stalls.txt (wave-time breakdown) "
+                        "from the two counter passes of STALL_COUNTERS (no GPU needed)")
+    p.add_argument("--num-cus", type=int, default=256, help="CUs of the measured GPU, for --write-mfma / --write-stalls")
     p.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                    help="write the traffic summary for --launches-only's workload from four rocprofv3 "
                         "counter_collection.csv files (no GPU needed)")
@@ -666,6 +669,75 @@ def write_mfma(workloads, scales, reps, pmc_csv, num_cus):
         print(path)
 
 
+# Where a GEMM's wave time goes: two rocprofv3 --pmc passes over
+# `bench.py --launches-only W1,W2,...` (each within one pass's hardware
+# limits: at most 8 SQ, 1 TA and 1 GRBM counter).
+STALL_COUNTERS = (
+    "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS "
+    "SQ_INSTS_VALU SQ_INSTS_LDS GRBM_GUI_ACTIVE TA_TA_BUSY",
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_SALU SQ_ACTIVE_INST_SCA SQ_LDS_CMD_FIFO_FULL "
+    "SQ_LDS_DATA_FIFO_FULL SQ_WAVES GRBM_GUI_ACTIVE",
+)
+
+
+def stalls_path(workload, scales="fp32"):
+    return os.path.join(PROFILES, f"gemm_kernel_{workload}{'_ue8m0' if scales == 'ue8m0' else ''}_stalls.txt")
+
+
+def write_stalls(workloads, scales, reps, csv_a, csv_b, num_cus):
+    """Wave-time breakdown of each workload's GEMM launches, medians over its
+    dispatches.  SQ_WAVE_CYCLES, SQ_WAIT_* and SQ_ACTIVE_INST_* count
+    quad-cycles summed over all waves, so their ratios are shares of the
+    waves' resident time: waiting at s_waitcnt or s_barrier (WAIT_ANY),
+    ready but not issued (WAIT_INST_ANY: the SIMD's issue port, the matrix
+    core or a dependency is busy), issuing VALU / LDS / scalar instructions.
+    The busy fractions divide by GRBM_GUI_ACTIVE per XCD (the kernel's
+    cycles) times the number of SIMDs, CUs or TA units."""
+    def med(path, counter):
+        return [v for v, _ in _per_workload(_counter_values(path, counter, "gemm_kernel"), workloads, reps, counter)]
+    a = {c: med(csv_a, c) for c in STALL_COUNTERS[0].split()}
+    b = {c: med(csv_b, c) for c in STALL_COUNTERS[1].split()}
+    cmd = _launch_cmd(workloads, scales, reps)
+    for i, wl in enumerate(workloads):
+        cyc = a["GRBM_GUI_ACTIVE"][i] / MI355X_XCDS
+        wave = a["SQ_WAVE_CYCLES"][i]
+        mfma = b["SQ_INSTS_MFMA"][i]
+        share = lambda c: a[c][i] / wave
+        lines = [
+            f"workload={wl}",
+            f"scales={scales}",
+            f"kernel_source_sha256_16={kernel_source_hash()}",
+            f"kernel_cycles={cyc:.6g}  (GRBM_GUI_ACTIVE per XCD, median of {reps} dispatches)",
+            f"waves={b['SQ_WAVES'][i]:.6g}",
+            "shares of resident wave time (SQ_WAVE_CYCLES):",
+            f"  wait_any={share('SQ_WAIT_ANY'):.3f}  (s_waitcnt / s_barrier: memory, LDS and barrier waits)",
+            f"  wait_inst_any={share('SQ_WAIT_INST_ANY'):.3f}  (ready, not issued: issue port, matrix core or dependency busy)",
+            f"  wait_inst_lds={share('SQ_WAIT_INST_LDS'):.3f}  (waiting to issue an LDS instruction)",
+            f"  active_valu={share('SQ_ACTIVE_INST_VALU'):.3f}  (VALU and MFMA issue)",
+            f"  active_lds={share('SQ_ACTIVE_INST_LDS'):.3f}",
+            f"  active_sca={b['SQ_ACTIVE_INST_SCA'][i] / wave:.3f}  (scalar; second pass)",
+            f"mfma_busy_frac={b['SQ_VALU_MFMA_BUSY_CYCLES'][i] / (b['GRBM_GUI_ACTIVE'][i] / MI355X_XCDS * 4 * num_cus):.4f}",
+            f"ta_busy_frac={a['TA_TA_BUSY'][i] / (cyc * num_cus):.4f}  (address unit feeding the LDS DMA, per CU)",
+            f"lds_cmd_fifo_full_frac={b['SQ_LDS_CMD_FIFO_FULL'][i] / (b['GRBM_GUI_ACTIVE'][i] / MI355X_XCDS * num_cus):.4f}"
+            f"  lds_data_fifo_full_frac={b['SQ_LDS_DATA_FIFO_FULL'][i] / (b['GRBM_GUI_ACTIVE'][i] / MI355X_XCDS * num_cus):.4f}",
+            f"mfma_insts={mfma:.6g}",
+            f"valu_insts_per_mfma={(a['SQ_INSTS_VALU'][i] - mfma) / mfma:.2f}  (SQ_INSTS_VALU counts the MFMAs too)",
+            f"lds_insts_per_mfma={a['SQ_INSTS_LDS'][i] / mfma:.2f}",
+            f"salu_insts_per_mfma={b['SQ_INSTS_SALU'][i] / mfma:.2f}",
+            "",
+            "commands (from the repository root, REPO = its absolute path):",
+            "  cd /tmp && export TMPDIR=/tmp",
+            f"  rocprofv3 --pmc {STALL_COUNTERS[0]} -f csv -d $REPO/gpurun_out/pmcs_a -o p -- python3 {cmd}",
+            f"  rocprofv3 --pmc {STALL_COUNTERS[1]} -f csv -d $REPO/gpurun_out/pmcs_b -o p -- python3 {cmd}",
+            f"  python3 {cmd.replace('$REPO/', '')} --write-stalls gpurun_out/pmcs_a/p_counter_collection.csv "
+            "gpurun_out/pmcs_b/p_counter_collection.csv",
+        ]
+        path = stalls_path(wl, scales)
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print(path)
+
+
 def _read_summary(path, key):
     """A value from a committed counter summary, or None if there is none or
     the kernel sources changed since it was taken."""
@@ -698,6 +770,11 @@ def main(argv=None):
         if not args.launches_only:
             raise SystemExit("--write-traffic needs --launches-only WORKLOADS")
         write_traffic(args.launches_only.split(","), args.scales, args.reps, *args.write_traffic)
+        return 0
+    if args.write_stalls:
+        if not args.launches_only:
+            raise SystemExit("--write-stalls needs --launches-only WORKLOADS")
+        write_stalls(args.launches_only.split(","), args.scales, args.reps, *args.write_stalls, args.num_cus)
         return 0
     if args.write_mfma:
         if not args.launches_only:

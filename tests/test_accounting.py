@@ -99,3 +99,50 @@ def test_counter_summaries_split_dispatches_per_workload(tmp_path, monkeypatch):
     assert got == {"w1": (200 * 2 + 10) * 1024, "w2": (1100 * 2 + 50) * 1024}
     with pytest.raises(SystemExit):
         bench.write_traffic(["w1", "w2", "w3"], "fp32", 3, f, wr, cf, cw)
+
+
+def test_stall_summary_shares(tmp_path, monkeypatch):
+    # Two --pmc passes over two workloads x 1 launch: the summary divides the
+    # wave-state counters by SQ_WAVE_CYCLES and the busy counters by the
+    # kernel's cycles per XCD times the units.
+    import csv
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    values_a = {"SQ_WAVE_CYCLES": 1000.0, "SQ_WAIT_ANY": 300.0, "SQ_WAIT_INST_ANY": 400.0, "SQ_WAIT_INST_LDS": 40.0,
+                "SQ_ACTIVE_INST_VALU": 190.0, "SQ_ACTIVE_INST_LDS": 30.0, "SQ_INSTS_VALU": 600.0,
+                "SQ_INSTS_LDS": 100.0, "GRBM_GUI_ACTIVE": 8 * 2000.0, "TA_TA_BUSY": 256 * 500.0}
+    values_b = {"SQ_VALU_MFMA_BUSY_CYCLES": 1024 * 1000.0, "SQ_INSTS_MFMA": 100.0, "SQ_INSTS_SALU": 250.0,
+                "SQ_ACTIVE_INST_SCA": 50.0, "SQ_LDS_CMD_FIFO_FULL": 256 * 100.0, "SQ_LDS_DATA_FIFO_FULL": 0.0,
+                "SQ_WAVES": 2048.0, "GRBM_GUI_ACTIVE": 8 * 2000.0}
+    assert set(values_a) == set(bench.STALL_COUNTERS[0].split())
+    assert set(values_b) == set(bench.STALL_COUNTERS[1].split())
+
+    def write_csv(path, values):
+        with open(path, "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            for d, scale in ((1, 1.0), (2, 2.0)):  # the second workload doubles every count
+                for c, v in values.items():
+                    w.writerow({"Dispatch_Id": d, "Kernel_Name": "gemm_kernel<x>", "Counter_Name": c,
+                                "Counter_Value": v * scale})
+
+    a, b = str(tmp_path / "a.csv"), str(tmp_path / "b.csv")
+    write_csv(a, values_a)
+    write_csv(b, values_b)
+    bench.write_stalls(["w1", "w2"], "fp32", 1, a, b, 256)
+    for wl in ("w1", "w2"):
+        text = open(bench.stalls_path(wl)).read()
+        fields = {}
+        for line in text.splitlines():
+            for tok in line.split():
+                if "=" in tok:
+                    k, v = tok.split("=", 1)
+                    fields[k] = v
+        assert float(fields["wait_any"]) == pytest.approx(0.3)
+        assert float(fields["wait_inst_any"]) == pytest.approx(0.4)
+        assert float(fields["active_valu"]) == pytest.approx(0.19)
+        assert float(fields["active_sca"]) == pytest.approx(0.05)
+        assert float(fields["mfma_busy_frac"]) == pytest.approx(0.5)
+        assert float(fields["ta_busy_frac"]) == pytest.approx(0.25)
+        assert float(fields["lds_cmd_fifo_full_frac"]) == pytest.approx(0.05)
+        assert float(fields["valu_insts_per_mfma"]) == pytest.approx(5.0)
+        assert float(fields["salu_insts_per_mfma"]) == pytest.approx(2.5)
