@@ -106,6 +106,9 @@ def parse_args(argv=None):
                    help="scale format: fp32 (default) or power-of-two exponent bytes (UE8M0)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work for the oracle sample")
+    p.add_argument("--probe-ceiling", action="store_true",
+                   help="run only the register-only loop probe (libdg_probe.so) and write "
+                        "profiles/mfma_loop_ceiling_gfx950.md")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain device copy of known size (for counter calibration)")
     p.add_argument("--launches-only", metavar="WORKLOADS",
@@ -738,6 +741,74 @@ def write_stalls(workloads, scales, reps, csv_a, csv_b, num_cus):
         print(path)
 
 
+PROBE_MODES = (("mfma_chains", "16 accumulating MFMA chains per wave (C = acc)"),
+               ("fp32_promotion", "per fragment row 4 MFMAs into partials, 1 scale multiply, 16 FMAs acc += P*s"),
+               ("block_scaled", "32 block-scaled MFMAs accumulating in the matrix core (UE8M0 form)"))
+FP8_FLOP_PER_CLK_PER_CU = 8192
+
+
+def probe_ceiling(torch, workgroups=256, iters=2000, reps=5):
+    """Run the register-only loop probe (libdg_probe.so, include/dg_probe.h)
+    for each mode at one and two waves per SIMD; write
+    profiles/mfma_loop_ceiling_gfx950.md and return its rows."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(__file__)), "moe_grouped_gemm_02_amd",
+                                   "libdg_probe.so"))
+    lib.dg_probe_loop.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.dg_probe_mfma_per_iter.argtypes = [ctypes.c_int]
+    rows = []
+    for mode, (name, what) in enumerate(PROBE_MODES):
+        for waves in (4, 8):
+            out = torch.empty(workgroups * waves * 64, dtype=torch.float32, device="cuda")
+            clk = torch.zeros(workgroups * 2, dtype=torch.int64, device="cuda")
+            stream = torch.cuda.current_stream()
+            times = []
+            for r in range(2 + reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                rc = lib.dg_probe_loop(mode, waves, workgroups, iters, ctypes.c_void_p(out.data_ptr()),
+                                       ctypes.c_void_p(clk.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+                e1.record(stream)
+                if rc != 0:
+                    raise RuntimeError(f"dg_probe_loop returned {rc}")
+                torch.cuda.synchronize()
+                if r >= 2:
+                    times.append(e0.elapsed_time(e1) * 1e-3)
+            if not bool(torch.isfinite(out).all()):
+                raise RuntimeError("probe accumulators not finite")
+            c = clk.view(-1, 2).double().cpu()
+            ghz = float(np.median((c[:, 0] / (c[:, 1] / 100e6)).numpy())) / 1e9
+            flops = workgroups * waves * iters * lib.dg_probe_mfma_per_iter(mode) * 2 * 16 * 16 * 128
+            t = float(np.median(times))
+            pf = flops / t / 1e15
+            at_clock = flops / t / (workgroups * FP8_FLOP_PER_CLK_PER_CU * ghz * 1e9)
+            rows.append({"mode": name, "what": what, "waves_per_simd": waves // 4, "pflops": round(pf, 3),
+                         "frac_of_5p0": round(pf / 5.0, 3), "clock_ghz": round(ghz, 3),
+                         "frac_at_measured_clock": round(at_clock, 3), "ms": round(t * 1e3, 3)})
+            print(json.dumps(rows[-1]), flush=True)
+    lines = [
+        "# Register-only loop ceilings on MI355X (gfx950): the GEMM inner loop's instruction mixes",
+        "",
+        "Command (from the repository root): `python3 bench.py --probe-ceiling`",
+        "",
+        f"Kernel: `probe_kernel<MODE>` of `moe_grouped_gemm_02_amd/csrc/dg_probe.hip` (libdg_probe.so), "
+        f"{workgroups} workgroups (one per CU), {iters} iterations; every operand in registers, no LDS or global "
+        "memory inside the timed loop. Time: median of "
+        f"{reps} launches (torch events, after 2 warm-up launches). Clock: median over workgroups of s_memtime "
+        "cycles / s_memrealtime (100 MHz) ticks over the loop. `frac_of_5p0` divides by the 5.0 PFLOP/s dense "
+        "FP8 peak (2.4 GHz); `frac_at_measured_clock` by 256 CUs x 8192 flop/clk x the measured clock.",
+        "",
+        "| mode | loop | waves per SIMD | PFLOP/s | of 5.0 PF | clock GHz | of peak at that clock |",
+        "|---|---|---:|---:|---:|---:|---:|",
+    ]
+    for r in rows:
+        lines.append(f"| {r['mode']} | {r['what']} | {r['waves_per_simd']} | {r['pflops']} | {r['frac_of_5p0']} | "
+                     f"{r['clock_ghz']} | {r['frac_at_measured_clock']} |")
+    with open(os.path.join(PROFILES, "mfma_loop_ceiling_gfx950.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return rows
+
+
 def _read_summary(path, key):
     """A value from a committed counter summary, or None if there is none or
     the kernel sources changed since it was taken."""
@@ -789,6 +860,9 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.probe_ceiling:
+        probe_ceiling(torch)
+        return 0
     import moe_grouped_gemm_02_amd as dg
 
     if args.calibrate_copy:

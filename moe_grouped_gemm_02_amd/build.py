@@ -8,6 +8,10 @@ a child process that preloads the sanitizer runtime.  Every source of both
 libraries compiles in its own process at once (objects under _build/), then
 each library is linked, so the second library adds little wall time.
 
+build() also compiles libdg_probe.so from dg_probe.hip: a register-only
+throughput probe of the GEMM inner loop's instruction mixes that the
+benchmark runs (bench.py --probe-ceiling).  libdg.so does not contain it.
+
 Every kernel is compiled for gfx950 only.  Flags:
 * -Xclang -target-feature -Xclang -packed-fp32-ops: no packed fp32 VALU ops
   (v_pk_fma_f32 and friends) in the generated code;
@@ -26,6 +30,10 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdg.so")
 ASAN_LIB = os.path.join(HERE, "libdg_host_asan.so")
+# The register-only loop probe (include/dg_probe.h), a measurement tool the
+# benchmark loads; the GEMM library does not contain it.
+PROBE_LIB = os.path.join(HERE, "libdg_probe.so")
+PROBE_SOURCES = ["dg_probe.hip"]
 SOURCES = ["dg_api.hip", "dg_quant.hip", "dg_gemm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -73,13 +81,13 @@ def build(verbose: bool = False, extra=None, host_asan: bool = True) -> str:
     """Compile libdg.so (and, unless host_asan is False, libdg_host_asan.so)
     in-tree and return the path of libdg.so; raises on failure."""
     os.makedirs(OBJ_DIR, exist_ok=True)
-    libs = [(LIB, "plain", list(extra or []))]
+    libs = [(LIB, "plain", list(extra or []), SOURCES), (PROBE_LIB, "plain", list(extra or []), PROBE_SOURCES)]
     if host_asan:
-        libs.append((ASAN_LIB, "host_asan", [*(extra or []), *HOST_SANITIZE]))
+        libs.append((ASAN_LIB, "host_asan", [*(extra or []), *HOST_SANITIZE], SOURCES))
     compiles, links = [], []
-    for lib, tag, flags in libs:
+    for lib, tag, flags, sources in libs:
         objs = []
-        for src in SOURCES:
+        for src in sources:
             obj = os.path.join(OBJ_DIR, f"{os.path.splitext(src)[0]}.{tag}.o")
             objs.append(obj)
             compiles.append((f"{src} ({tag})", [HIPCC, *FLAGS, *flags, "-I", INCLUDE, "-I", CSRC, "-c",
@@ -93,7 +101,7 @@ def build(verbose: bool = False, extra=None, host_asan: bool = True) -> str:
         raise RuntimeError("\n".join(failed))
     if verbose and notes:
         print("\n".join(notes))
-    for lib, _, _ in libs:
+    for lib, _, _, _ in libs:
         os.replace(lib + ".tmp", lib)
     return LIB
 

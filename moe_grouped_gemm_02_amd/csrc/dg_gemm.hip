@@ -658,8 +658,9 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
       // Two-stage tiles (the 256x256 one) with power-of-two scales place the
       // slice barrier before the last fragment row and prefetch the next
       // slice's operands across it (measured: 9% faster at 4096x4096x7168).
-      // With fp32 scales the same loop measured no faster: the promotion
-      // FMAs, not the barrier, set the pace there.
+      // With fp32 scales the same loop spills inside the K loop: across the
+      // last row the promotion's partial registers, the slice's A fragment
+      // and the next slice's B fragments are live together.
       constexpr bool kLate = T::STAGES == 2 && SF == kScaleUE8M0;
       if constexpr (kLate) {
         static_assert(T::FM >= 2 && !T::kPipe, "the late barrier sits between two fragment rows");

@@ -47,3 +47,26 @@ def test_more_than_one_gpu_is_refused():
     r = _run(["--gpus", "2"], timeout=60)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+@pytest.mark.gpu
+def test_loop_probe_runs_every_mode():
+    # The register-only loop probe (libdg_probe.so) behind bench.py
+    # --probe-ceiling: every mode at one and two waves per SIMD writes finite
+    # sums for every thread and a positive cycle and tick count per workgroup.
+    import ctypes
+
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "moe_grouped_gemm_02_amd", "libdg_probe.so"))
+    lib.dg_probe_loop.argtypes = [ctypes.c_int] * 4 + [ctypes.c_void_p] * 3
+    for mode in (0, 1, 2):
+        for waves in (4, 8):
+            wgs = 8
+            out = torch.full((wgs * waves * 64,), float("nan"), dtype=torch.float32, device="cuda")
+            clk = torch.zeros(wgs * 2, dtype=torch.int64, device="cuda")
+            rc = lib.dg_probe_loop(mode, waves, wgs, 20, out.data_ptr(), clk.data_ptr(),
+                                   torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            assert rc == 0
+            assert bool(torch.isfinite(out).all()) and bool((out > 0).all()), (mode, waves)
+            assert bool((clk > 0).all()), (mode, waves)
