@@ -552,13 +552,24 @@ KERNEL_SOURCES = ("dg_gemm.hip", "dg_device.h", "dg_internal.h")
 COPY_BYTES = 256 << 20
 
 
+def _strip_comments(text):
+    """C++ source without its // and /* */ comments and with runs of
+    whitespace collapsed, so that editing a comment keeps the hash."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
+    """Hash of the GEMM kernel sources' code (comments excluded): counter
+    summaries taken from other code are not reported."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "moe_grouped_gemm_02_amd", "csrc")
     for name in KERNEL_SOURCES:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(_strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -10,13 +10,17 @@
 // gfx950 mapping
 // * One v_mfma_f32_16x16x128_f8f6f4 covers exactly one 128-deep scale slice of
 //   a 16x16 output fragment, so a partial product never mixes two slices:
-//   P = mfma(a, b, 0), then acc += P * (sa * sb) on the VALU, per lane for its
-//   4 rows x 1 column.
+//   P = mfma(b, a, 0) (the B fragment as the first operand), then
+//   acc += P * (sa * sb) on the VALU, per lane for its 1 row x 4 columns, so
+//   one activation scale serves the lane's four results.
 // * Fragment layouts (64-wide wavefronts).  Operand: lane l holds 32 bytes of
 //   K for row (l % 16), lane group l / 16 selects which 32 bytes; A and B use
 //   the same K assignment, so the contraction is the full 128-term dot product
-//   whatever order the matrix core visits the bytes in.  Result: lane l holds
-//   column (l % 16), rows 4 * (l / 16) + i, i = 0..3.
+//   whatever order the matrix core visits the bytes in.  Result of
+//   mfma(b, a): lane l holds output row (l % 16) of the A fragment, columns
+//   4 * (l / 16) + i, i = 0..3.  The K-grouped GEMM, whose B scales are per
+//   column, keeps mfma(a, b): lane l holds column (l % 16), rows
+//   4 * (l / 16) + i.
 // * Operands are staged HBM -> LDS with global_load_lds_dwordx4 (no register
 //   staging), STAGES deep, one barrier per K slice.  A stage holds the A tile
 //   [BM][128], the B tile [BN][128] and the BM activation scales of the slice.

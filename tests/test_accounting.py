@@ -146,3 +146,13 @@ def test_stall_summary_shares(tmp_path, monkeypatch):
         assert float(fields["lds_cmd_fifo_full_frac"]) == pytest.approx(0.05)
         assert float(fields["valu_insts_per_mfma"]) == pytest.approx(5.0)
         assert float(fields["salu_insts_per_mfma"]) == pytest.approx(2.5)
+
+
+def test_kernel_source_hash_ignores_comments_only():
+    # Counter summaries carry the hash of the kernel code they were taken
+    # from; editing a comment keeps it, editing code changes it.
+    code = "int f(int x) {\n  return x + 1;  // one more\n}\n/* block\n comment */\n"
+    assert bench._strip_comments(code) == bench._strip_comments(code.replace("one more", "add one"))
+    assert bench._strip_comments(code) == bench._strip_comments(code.replace("block\n comment", "other"))
+    assert bench._strip_comments(code) != bench._strip_comments(code.replace("x + 1", "x + 2"))
+    assert "one more" not in bench._strip_comments(code) and "return x + 1;" in bench._strip_comments(code)
