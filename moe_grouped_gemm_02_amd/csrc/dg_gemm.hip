@@ -101,17 +101,17 @@ __device__ __forceinline__ void barrier_all() { asm volatile("s_barrier" : : : "
 
 // Wait until at most NEWER stages of this wave's DMAs are in flight (the
 // stages issued after the one the loop needs next).  Waves issue different
-// numbers of DMAs per stage (T::dmas_of_wave), so the count is picked per
-// run of waves with equal counts.
-template <class T, int NEWER, int W = 0>
+// numbers of DMAs per stage (DmaPlan P::dmas_of_wave), so the count is
+// picked per run of waves with equal counts.
+template <class P, int NEWER, int W = 0>
 __device__ __forceinline__ void wait_stage(int wave) {
-  if constexpr (W + 1 >= T::kWaves) {
-    wait_vm<NEWER * T::dmas_of_wave(W)>();
-  } else if constexpr (T::dmas_of_wave(W + 1) == T::dmas_of_wave(W)) {
-    wait_stage<T, NEWER, W + 1>(wave);
+  if constexpr (W + 1 >= P::kWaves) {
+    wait_vm<NEWER * P::dmas_of_wave(W)>();
+  } else if constexpr (P::dmas_of_wave(W + 1) == P::dmas_of_wave(W)) {
+    wait_stage<P, NEWER, W + 1>(wave);
   } else {
-    if (wave <= W) wait_vm<NEWER * T::dmas_of_wave(W)>();
-    else wait_stage<T, NEWER, W + 1>(wave);
+    if (wave <= W) wait_vm<NEWER * P::dmas_of_wave(W)>();
+    else wait_stage<P, NEWER, W + 1>(wave);
   }
 }
 
@@ -242,21 +242,10 @@ struct Tile {
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
   static constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 fragments per wave
-  // DMA instruction i of a stage fills LDS bytes [1024 i, 1024 i + 1024).
-  // Instruction i = j * kWaves + wave, so every wave's j-th instruction falls
-  // in the same region (A rows, B rows, scales) - a compile-time choice.
+  // DMA instruction i of a stage fills LDS bytes [1024 i, 1024 i + 1024)
+  // (how the instructions are split over the waves: DmaPlan below).
   static constexpr int kAInstr = BM / 8;            // 1 KB DMA instructions per slice
   static constexpr int kBInstr = BN / 8;
-  // Per-wave instruction rounds: wave w issues A instructions j * kWaves + w
-  // for j < kAJ while that index is below kAInstr (the last round may be
-  // partial when the tile's rows do not split evenly over the waves), then
-  // the B instructions the same way.
-  static constexpr int kAJ = (kAInstr + kWaves - 1) / kWaves;
-  static constexpr int kBJ = (kBInstr + kWaves - 1) / kWaves;
-  static constexpr int kLPW = kAJ + kBJ;            // A/B DMA rounds per wave per stage; waves 0
-                                                    // and 1 issue one more each, for the
-                                                    // activation and the weight scales
-  static constexpr int kIssue = kLPW + 1;           // DMA pieces per wave per stage
   // Fragment rows over which a stage's DMA pieces are spread (0: all of
   // them right after the barrier, before any compute).  Spreading pays with
   // two waves per SIMD, where the other wave keeps the SIMD busy while one
@@ -269,12 +258,6 @@ struct Tile {
   static constexpr int kSBOff = (kAInstr + kBInstr + 1) * 1024;  // weight scales of the slice
   static constexpr int kSBBytes = SB_BYTES;
   static constexpr int kStageBytes = (kAInstr + kBInstr + 1) * 1024 + SB_BYTES;
-  // DMA instructions wave w issues per stage: its A and B instructions plus,
-  // for waves 0 and 1, the scale DMA.
-  static constexpr int dmas_of_wave(int w) {
-    return (kAInstr / kWaves + (w < kAInstr % kWaves ? 1 : 0)) + (kBInstr / kWaves + (w < kBInstr % kWaves ? 1 : 0)) +
-           (w < 2 ? 1 : 0);
-  }
   static constexpr int kBOff = BM * 128;
   static constexpr int kSOff = (BM + BN) * 128;
   static constexpr bool kOneSB = (128 % TN) == 0;   // wave columns inside one 128-block
@@ -288,6 +271,33 @@ struct Tile {
   static_assert(STAGES >= 2, "need two stages");
   static_assert(kWaves >= 2, "waves 0 and 1 load the scales");
   static_assert(STAGES * kStageBytes + 16 <= 160 * 1024, "LDS overflow");
+};
+
+// How a stage's A/B DMA instructions are split over a tile's waves: the first
+// DW waves issue them, wave w the instructions j * DW + w for j < kAJ while
+// that index is below kAInstr (the last round may be partial when the rows
+// do not split evenly), then the B instructions the same way; so every
+// wave's j-th instruction falls in the same region (A rows, B rows) - a
+// compile-time choice.  Waves 0 and 1 also issue the activation- and
+// weight-scale DMA.  DW = kWaves spreads the work over every wave; the
+// fp32-scale 256 x 256 tile uses DW = 4, one issuing wave per SIMD, so each
+// SIMD keeps a wave that never waits on the vector-memory address unit while
+// a stage goes out (see kDmaWaves).
+template <class T, int DW>
+struct DmaPlan {
+  static_assert(DW >= 2 && DW <= T::kWaves, "waves 0 and 1 issue the scale DMAs");
+  static constexpr int kWaves = T::kWaves;
+  static constexpr int kDW = DW;
+  static constexpr int kAJ = (T::kAInstr + DW - 1) / DW;
+  static constexpr int kBJ = (T::kBInstr + DW - 1) / DW;
+  static constexpr int kLPW = kAJ + kBJ;  // A/B DMA rounds per issuing wave per stage
+  static constexpr int kIssue = kLPW + 1;  // DMA pieces per wave per stage (the last: scales)
+  // DMA instructions wave w issues per stage.
+  static constexpr int dmas_of_wave(int w) {
+    return (w < DW ? (T::kAInstr / DW + (w < T::kAInstr % DW ? 1 : 0)) + (T::kBInstr / DW + (w < T::kBInstr % DW ? 1 : 0))
+                   : 0) +
+           (w < 2 ? 1 : 0);
+  }
 };
 
 // Decode a linear work-unit index into a tile.  XCD-aware: workgroup w runs on
@@ -350,6 +360,13 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
     return kTr ? __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, 0, 0, eb, 0, ea)
                : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
   };
+  // The split of each stage's DMAs over the waves.  With fp32 scales the
+  // 8-wave 256 x 256 tile lets only waves 0-3 (one per SIMD) issue them: the
+  // SIMD's other wave keeps the matrix core fed while a stage goes out through
+  // the address unit (back to back: masked 4x1024x4096x7168 114-116 ->
+  // 110-112 us, 4096x32768x512 151 -> 145-146 us, contiguous 973 -> 964-970
+  // us).  The UE8M0 loop spills with that split and keeps all eight.
+  using DP = DmaPlan<T, (SF == kScaleF32 && T::kWaves == 8 && T::BM * T::BN >= 256 * 256) ? 4 : T::kWaves>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::STAGES * T::kStageBytes];
   __shared__ int last_flag;
 
@@ -556,16 +573,17 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
       // Stage loader.  DMA instruction i of a stage fills LDS bytes
       // [1024 i, 1024 i + 1024): instructions [0, BM/8) carry A rows,
       // [BM/8, (BM+BN)/8) B rows, then the BM activation scales and the
-      // weight scales.  A wave's share of a stage is kLPW A/B instructions
-      // plus, for waves 0 and 1, one scale instruction: piece j of
-      // kIssue = kLPW + 1 (a compile-time index; the last piece is the scale
-      // DMA, empty for waves 2 and up).
+      // weight scales.  An issuing wave's share of a stage is DP::kLPW A/B
+      // instructions plus, for waves 0 and 1, one scale instruction: piece j
+      // of DP::kIssue = kLPW + 1 (a compile-time index; the last piece is the
+      // scale DMA, empty for waves 2 and up).
       auto issue_piece = [&](int kb, int buf, auto jc) {
         constexpr int j = decltype(jc)::value;
         const uint32_t stage_lds = smem_base + buf * T::kStageBytes;
-        if constexpr (j < T::kAJ) {
-          const int instr = j * T::kWaves + wave;
-          if (T::kAInstr % T::kWaves != 0 && instr >= T::kAInstr) return;  // partial last round
+        if constexpr (j < DP::kAJ) {
+          if (DP::kDW < T::kWaves && wave >= DP::kDW) return;  // not an issuing wave
+          const int instr = j * DP::kDW + wave;
+          if (T::kAInstr % DP::kDW != 0 && instr >= T::kAInstr) return;  // partial last round
           const int q = instr * 64 + lane;
           if constexpr (kAT) {
             // K row kr of the slice, chunk position cp; the chunk holds rows
@@ -584,11 +602,12 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
             // The slice advances the uniform base; the per-lane offset is fixed.
             dma16(stage_lds + instr * 1024, A + kb * 128, (uint32_t)gr * (uint32_t)p.lda + c * 16);
           }
-        } else if constexpr (j < T::kLPW) {
-          constexpr int jb = j - T::kAJ;
-          if (T::kBInstr % T::kWaves != 0 && jb * T::kWaves + wave >= T::kBInstr) return;  // partial last round
-          const int instr = T::kAInstr + jb * T::kWaves + wave;
-          const int q = (jb * T::kWaves + wave) * 64 + lane;
+        } else if constexpr (j < DP::kLPW) {
+          constexpr int jb = j - DP::kAJ;
+          if (DP::kDW < T::kWaves && wave >= DP::kDW) return;  // not an issuing wave
+          if (T::kBInstr % DP::kDW != 0 && jb * DP::kDW + wave >= T::kBInstr) return;  // partial last round
+          const int instr = T::kAInstr + jb * DP::kDW + wave;
+          const int q = (jb * DP::kDW + wave) * 64 + lane;
           if constexpr (kBT) {
             constexpr int C = T::BN / 16;
             const int kr = q / C, c = (q % C) ^ mn_swizzle<T::BN>(q / C);
@@ -596,7 +615,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
             dma16(stage_lds + instr * 1024, B + (size_t)(kb * 128) * (size_t)p.ldb,
                   (uint32_t)kr * (uint32_t)p.ldb + (uint32_t)gn);
           } else {
-            const int r = kmaj_dma_row(jb * T::kWaves + wave, lane), c = (lane & 7) ^ (r & 7);
+            const int r = kmaj_dma_row(jb * DP::kDW + wave, lane), c = (lane & 7) ^ (r & 7);
             const int gn = min(n0 + r, p.n - 1);
             dma16(stage_lds + instr * 1024, B + kb * 128, (uint32_t)gn * (uint32_t)p.ldb + c * 16);
           }
@@ -637,7 +656,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
         }
       };
       auto issue_stage = [&](int kb, int buf) {
-        static_for<T::kIssue>([&](auto jc) { issue_piece(kb, buf, jc); });
+        static_for<DP::kIssue>([&](auto jc) { issue_piece(kb, buf, jc); });
       };
       // The pieces that go out after the MFMAs of fragment row i, spreading a
       // stage's DMAs over the compute of the previous one: the vector-memory
@@ -645,9 +664,9 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
       // issued its whole share at once would sit idle behind the queue.
       auto issue_row = [&](int kb, int buf, auto ic) {
         constexpr int i = decltype(ic)::value;
-        static_for<T::kIssue>([&](auto jc) {
+        static_for<DP::kIssue>([&](auto jc) {
           constexpr int j = decltype(jc)::value;
-          if constexpr (j * T::kSpreadRows / T::kIssue == i) issue_piece(kb, buf, jc);
+          if constexpr (j * T::kSpreadRows / DP::kIssue == i) issue_piece(kb, buf, jc);
         });
       };
 
@@ -685,16 +704,16 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
         // last row: piece q goes out after column q * FN / kIssue.
         auto issue_after = [&](int kb, int buf, auto jc) {
           constexpr int j = decltype(jc)::value;
-          static_for<T::kIssue>([&](auto qc) {
+          static_for<DP::kIssue>([&](auto qc) {
             constexpr int q = decltype(qc)::value;
-            if constexpr (q * T::FN / T::kIssue == j) issue_piece(kb, buf, qc);
+            if constexpr (q * T::FN / DP::kIssue == j) issue_piece(kb, buf, qc);
           });
         };
         static_assert(SF == kScaleUE8M0, "the late-barrier loop is the power-of-two-scale one");
         if (nkb > 0) issue_stage(kb_at(0), 0);
         if (nkb > 1) {
           issue_stage(kb_at(1), 1);
-          wait_stage<T, 1>(wave);
+          wait_stage<DP, 1>(wave);
         } else {
           wait_vm<0>();
         }
@@ -770,7 +789,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
           // Wait for this wave's DMAs of stage `it` (newer stages may stay in
           // flight), then barrier so every wave's part of the stage has landed.
           if (it + T::STAGES - 2 < nkb) {
-            wait_stage<T, T::STAGES - 2>(wave);
+            wait_stage<DP, T::STAGES - 2>(wave);
           } else {
             wait_vm<0>();
           }
