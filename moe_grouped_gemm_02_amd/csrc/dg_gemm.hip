@@ -361,12 +361,15 @@ __global__ __launch_bounds__(T::kThreads) void gemm_kernel(GemmParams p, Schedul
                : __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
   };
   // The split of each stage's DMAs over the waves.  With fp32 scales the
-  // 8-wave 256 x 256 tile lets only waves 0-3 (one per SIMD) issue them: the
-  // SIMD's other wave keeps the matrix core fed while a stage goes out through
-  // the address unit (back to back: masked 4x1024x4096x7168 114-116 ->
-  // 110-112 us, 4096x32768x512 151 -> 145-146 us, contiguous 973 -> 964-970
-  // us).  The UE8M0 loop spills with that split and keeps all eight.
-  using DP = DmaPlan<T, (SF == kScaleF32 && T::kWaves == 8 && T::BM * T::BN >= 256 * 256) ? 4 : T::kWaves>;
+  // 8-wave 256-row tiles (256 x 256 and 256 x 160) let only waves 0-3 (one
+  // per SIMD) issue them: the SIMD's other wave keeps the matrix core fed
+  // while a stage goes out through the address unit (back to back: masked
+  // 4x1024x4096x7168 114-116 -> 110-112 us, 4096x32768x512 151 -> 145-146
+  // us, contiguous 973 -> 964-970 us, 4096x2112x7168 on 256 x 160 tiles
+  // 95-97 -> 90.5-92 us).  The UE8M0 loop spills with that split and keeps
+  // all eight; on the 8-wave 128 x 128 decode tile it measured mixed
+  // (128x32768x512 11.0 -> 12.1 us, 128x7168x16384 37.2 -> 36.7 us).
+  using DP = DmaPlan<T, (SF == kScaleF32 && T::kWaves == 8 && T::BM == 256) ? 4 : T::kWaves>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::STAGES * T::kStageBytes];
   __shared__ int last_flag;
 
