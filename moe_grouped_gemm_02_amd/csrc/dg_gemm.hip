@@ -280,9 +280,9 @@ struct Tile {
 // wave's j-th instruction falls in the same region (A rows, B rows) - a
 // compile-time choice.  Waves 0 and 1 also issue the activation- and
 // weight-scale DMA.  DW = kWaves spreads the work over every wave; the
-// fp32-scale 256 x 256 tile uses DW = 4, one issuing wave per SIMD, so each
-// SIMD keeps a wave that never waits on the vector-memory address unit while
-// a stage goes out (see kDmaWaves).
+// fp32-scale 8-wave 256-row tiles use DW = 4, one issuing wave per SIMD, so
+// each SIMD keeps a wave that never waits on the vector-memory address unit
+// while a stage goes out (the plan `DP` chosen in gemm_kernel).
 template <class T, int DW>
 struct DmaPlan {
   static_assert(DW >= 2 && DW <= T::kWaves, "waves 0 and 1 issue the scale DMAs");
